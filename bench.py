@@ -1,0 +1,229 @@
+"""Benchmark of the NVFP4 paged-KV hot path on one MI355X.
+
+One step = one attention layer of a 2048x2048 causal prefill with
+Qwen3-8B-shaped attention (1 request, q_len = kv_len = 2048, 32 query heads,
+8 KV heads, head_dim 128, page size 16): append the 2048 new K/V rows to the
+NVFP4 paged cache through the slot mapping, then run the causal paged
+prefill over those pages.  The plan step runs once per batch (as in a
+serving engine, where one plan serves every layer) and its host time is
+reported separately.
+
+Prints one JSON line.  `value` is causal-prefill TFLOP/s over the whole step
+(algorithmic flops 4 * head_dim * allowed (query, key) pairs per query head,
+divided by the step time).  Also reported: per-kernel times from HIP events
+on the launch stream, the roofline of the dominant kernel, the append's
+achieved GB/s on this workload and on the 65,536-token append stress
+workload, and the CPU oracle timed on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal prefill TFLOP/s + append GB/s on NVFP4 paged KV (% of MI355X roofline)"
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("prefill.hip", "append.hip", "nvfp4kv_codec.hpp"):
+        h.update(open(os.path.join(ROOT, "nvfp4_paged_kv_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def attention_flops(q_lens, kv_lens, num_q_heads, head_dim):
+    """4 * D * sum over requests, query heads and query rows of the allowed keys."""
+    tot = 0
+    for lq, lk in zip(q_lens, kv_lens):
+        lq, lk = int(lq), int(lk)
+        tot += lq * (lk - lq) + lq * (lq + 1) // 2
+    return 4 * head_dim * num_q_heads * tot
+
+
+def append_bytes(tokens, heads, d):
+    """bf16 K and V read + packed NVFP4 and scale bytes written + int64 slots."""
+    return tokens * heads * (2 * d + d // 2 + d // 16) * 2 + 8 * tokens
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-append-stress", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(each step's work is one GPU's share; see the design notes on sharding).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import nvfp4_paged_kv_amd as K
+    import workloads as W
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = W.prefill_2k(dev)
+    cache = K.PagedCache.empty(w.num_pages, w.page_size, w.num_kv_heads, w.head_dim, dev,
+                               w.k_scale, w.v_scale)
+    qo_h, kvl_h = torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens)
+    kvp_h = torch.from_numpy(w.kv_indptr)
+    qo_d, kvl_d = qo_h.to(dev), kvl_h.to(dev)
+    kvp_d, pt_d = kvp_h.to(dev), torch.from_numpy(w.page_table).to(dev)
+    out = torch.empty_like(w.q)
+
+    t0 = time.perf_counter()
+    nplan = 200
+    for _ in range(nplan):
+        plan = K.plan(qo_h, kvl_h, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                      kv_indptr=kvp_h)
+    plan_us = (time.perf_counter() - t0) / nplan * 1e6
+
+    def step():
+        cache.append(w.k, w.v, w.slot_mapping)
+        K.paged_prefill_causal(w.q, qo_d, kvp_d, pt_d, kvl_d, cache, out, w.sm_scale, plan=plan)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # timed region: K steps, bracketed by device synchronization
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) / args.steps * 1e3
+    bits = K.read_device_error(dev)
+    if bits:
+        raise SystemExit(f"device error bits {bits}")
+
+    # per-kernel durations: HIP events on the launch stream (torch's current stream)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in ev:
+        e[0].record()
+        cache.append(w.k, w.v, w.slot_mapping)
+        e[1].record()
+        K.paged_prefill_causal(w.q, qo_d, kvp_d, pt_d, kvl_d, cache, out, w.sm_scale, plan=plan)
+        e[2].record()
+    torch.cuda.synchronize()
+    app_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    pre_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+
+    flops = attention_flops(w.q_lens, w.kv_lens, w.num_q_heads, w.head_dim)
+    abytes = append_bytes(int(w.kv_lens.sum()), w.num_kv_heads, w.head_dim)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    pre_tflops = flops / (pre_ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        t = json.load(open(TRAFFIC_FILE))
+        if t.get("kernel_source_hash") == kernel_source_hash():
+            traffic = t.get("prefill_2k", {}).get("bytes_per_launch")
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": 1, "q_len": 2048, "kv_len": 2048,
+                   "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128, "page_size": 16,
+                   "kv_format": "nvfp4 (e2m1 + e4m3 per 16, fp32 global scale)",
+                   "step": "append 2048 K/V rows + causal paged prefill",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel<128,4>",
+                     "achieved": round(pre_tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic, "flops_per_launch": flops,
+                     "avg_launch_us": round(pre_ms * 1e3, 2)},
+        "append": {"bound": "hbm", "bytes_per_launch": abytes, "avg_launch_us": round(app_ms * 1e3, 2),
+                   "achieved_GBps": round(abytes / (app_ms * 1e-3) / 1e9, 1), "peak_GBps": HBM_PEAK_GBS,
+                   "frac": round(abytes / (app_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "plan_host_us": round(plan_us, 2),
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    del ev
+    if not args.no_append_stress:
+        result["append_stress"] = bench_append_stress(K, W, dev, torch, np)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, flops)
+    print(json.dumps(result), flush=True)
+
+
+def bench_append_stress(K, W, dev, torch, np, iters=12):
+    """65,536-token append (Student-t(3) values, scattered slots).  The 256 MB
+    Infinity Cache is flushed (a 512 MiB write, untimed) before every timed
+    launch; median of 12 launches, HIP events on the launch stream."""
+    a = W.append_stress(dev)
+    cache = K.PagedCache.empty(a.num_pages, a.page_size, a.num_kv_heads, a.head_dim, dev,
+                               a.k_scale, a.v_scale)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        cache.append(a.k, a.v, a.slot_mapping)
+    times = []
+    for _ in range(iters):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        cache.append(a.k, a.v, a.slot_mapping)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    nbytes = append_bytes(a.k.shape[0], a.num_kv_heads, a.head_dim)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": a.name, "bound": "hbm", "bytes_per_launch": nbytes,
+            "median_launch_us": round(ms * 1e3, 2), "achieved_GBps": round(gbs, 1),
+            "peak_GBps": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4), "cache": "cold (flushed)"}
+
+
+def cpu_baseline(w, flops_full):
+    """The oracle (plain C, fp64 attention) on a bounded sample of the same
+    step: append of all 2048 K/V rows and the prefill of 2 of the 8 KV heads
+    (8 of 32 query heads); TFLOP/s over the sample's algorithmic flops."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+    import workloads as W
+    hk_s = 2
+    G = w.num_q_heads // w.num_kv_heads
+    q = W.bf16_bits(w.q[:, : hk_s * G])
+    k, v = W.bf16_bits(w.k), W.bf16_bits(w.v)
+    slots = w.slot_mapping.cpu().numpy()
+    P, ps, H, D = w.num_pages, w.page_size, w.num_kv_heads, w.head_dim
+    threads = O._threads()
+    t0 = time.perf_counter()
+    c = [np.zeros((P, ps, H, D // 2), np.uint8), np.zeros((P, ps, H, D // 2), np.uint8),
+         np.zeros((P, ps, H, D // 16), np.uint8), np.zeros((P, ps, H, D // 16), np.uint8)]
+    O.append(k, v, slots, w.k_scale, w.v_scale, *c, ps, nthreads=threads)
+    c = [np.ascontiguousarray(x[:, :, :hk_s]) for x in c]
+    O.prefill(q, w.qo_indptr, w.kv_indptr, w.page_table, w.kv_lens, *c, w.k_scale, w.v_scale,
+              hk_s * G, w.sm_scale, nthreads=threads)
+    sec = time.perf_counter() - t0
+    flops = flops_full * hk_s // w.num_kv_heads
+    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": round(sec, 3),
+            "sample": f"append of all 2048 K/V rows + causal prefill of {hk_s} of 8 KV heads "
+                      f"({hk_s * G} of 32 query heads), fp64 oracle"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,202 @@
+/*
+ * nvfp4kv.h -- C ABI of the MI355X (gfx950) NVFP4 paged-KV library:
+ * NVFP4 quantize + append into a paged KV cache through a slot mapping, and
+ * batched causal prefill attention that reads those NVFP4 pages.
+ *
+ * Sources: the FlashInfer pull-request analysis pages
+ *   [PR #6204] "NVFP4 KV cache append: removing the host sync" (append API,
+ *              device global scales checked in the kernel, no host sync),
+ *   [PR #4769] "NVFP4 KV tile repack" (prefill over NVFP4 KV, dequantize each
+ *              KV tile once into a 16-bit staging tile),
+ *   [PR #3575] "FP8 causal attention: O(1) tile decode and global scheduling"
+ *              (uniform-length flag, heaviest-first Q tiles, L2 gate),
+ *   [PR #5043] "plan(): Python max() to Tensor.max()" (plan-step max lengths
+ *              from vectorised reductions, lengths cast to int32).
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless the name ends in `_host`.  All
+ *     buffers belong to the caller; the library allocates nothing and keeps no
+ *     state besides a per-device property cache.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns: none synchronizes the host, except
+ *     nvfp4kv_read_device_error, which exists to do exactly that.
+ *   - Problems the host can see without reading device memory return a
+ *     negative status before anything is enqueued.  Problems only the device
+ *     can see (bad device scales, out-of-range slots or page ids) set bits in
+ *     the caller's 32-bit device error word `dev_error` (atomic OR).
+ *   - Element types: bf16 = IEEE bfloat16 bit patterns (2 bytes).
+ *
+ * NVFP4 cache format (readings of the pages, which do not fix a layout):
+ *   - a block is 16 consecutive head_dim elements of one (token, head);
+ *     element value = e2m1(code) * E4M3(sf) * g, g the tensor's global
+ *     decode scale (k_scale or v_scale);
+ *   - E2M1 codes are 4 bits (bit 3 = sign), two per byte, the even element in
+ *     the low nibble; scale factors are OCP E4M3FN bytes (unsigned use);
+ *   - NHD pages: cache   uint8 [num_pages][page_size][num_kv_heads][head_dim/2]
+ *                scales  uint8 [num_pages][page_size][num_kv_heads][head_dim/16]
+ *   - slot s names cache row s: page s / page_size, offset s % page_size.
+ */
+#ifndef NVFP4KV_H
+#define NVFP4KV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every call. */
+enum {
+  NVFP4KV_OK = 0,
+  NVFP4KV_EINVAL = -1,        /* null pointer, bad size, misaligned pointer */
+  NVFP4KV_EUNSUPPORTED = -2,  /* shape this build has no kernel for */
+  NVFP4KV_ERANGE = -3,        /* host-visible length inconsistency (q_len > kv_len, ...) */
+  NVFP4KV_EHIP = -4,          /* the HIP runtime reported an error */
+  NVFP4KV_EWORKSPACE = -5     /* workspace missing or smaller than plan->workspace_bytes */
+};
+
+/* Bits of the device error word. */
+enum {
+  NVFP4KV_DEV_BAD_K_SCALE = 1u, /* k_scale not positive finite: the append wrote nothing */
+  NVFP4KV_DEV_BAD_V_SCALE = 2u, /* v_scale not positive finite: the append wrote nothing */
+  NVFP4KV_DEV_SLOT_OOB = 4u,    /* a slot >= num_pages * page_size: that row was skipped */
+  NVFP4KV_DEV_PAGE_OOB = 8u,    /* a page id outside [0, num_pages): read as zeros */
+  NVFP4KV_DEV_BAD_SCALE_ATTN = 16u /* the prefill saw a non positive-finite k/v scale */
+};
+
+/*
+ * nvfp4_append_paged_kv -- quantize new K/V rows to NVFP4 and write them into
+ * the paged cache at the slots slot_mapping names.  [PR #6204] introduction
+ * and append-function section; the scale contract is its docstring section.
+ *
+ *   k, v          bf16 [num_tokens][num_kv_heads][head_dim], contiguous,
+ *                 16-byte aligned.
+ *   slot_mapping  int64 [num_tokens]; slot < 0 = padding row (skipped);
+ *                 slot >= num_pages*page_size sets NVFP4KV_DEV_SLOT_OOB and
+ *                 the row is skipped.  Two tokens with one slot: unspecified
+ *                 which one wins.
+ *   k_scale, v_scale  device fp32 scalars: global decode scales.  Checked by
+ *                 the kernel, never read by the host.  If either is not
+ *                 positive finite the kernel sets NVFP4KV_DEV_BAD_K_SCALE /
+ *                 _BAD_V_SCALE and writes nothing at all.
+ *   k_cache, v_cache, k_sf, v_sf  the NHD cache and scale pages (see above);
+ *                 k_cache/v_cache 8-byte aligned.  Only the addressed rows
+ *                 are written.
+ *   dev_error     device uint32 error word (required).
+ * Block quantizer (fp32, fixed order): a = max|x_i| (NaN ignored);
+ * s = a / (6 g); sf = E4M3 round-to-nearest-even of s, saturating at 448;
+ * r = sf ? 1/(E4M3(sf) g) : 0; code_i = sign(x_i) | E2M1 round-to-nearest-
+ * even of x_i r, saturating at 6 (NaN -> magnitude 0).
+ * num_tokens == 0: returns NVFP4KV_OK, enqueues nothing and checks nothing
+ * (the scales included).
+ */
+int nvfp4_append_paged_kv(const void* k, const void* v, const int64_t* slot_mapping,
+                          int64_t num_tokens, const float* k_scale, const float* v_scale,
+                          uint8_t* k_cache, uint8_t* v_cache, uint8_t* k_sf, uint8_t* v_sf,
+                          int64_t num_pages, int32_t page_size, int32_t num_kv_heads,
+                          int32_t head_dim, uint32_t* dev_error, void* stream);
+
+/* One NVFP4 paged cache: K and V share the geometry. */
+typedef struct {
+  const uint8_t* k_cache; /* [num_pages][page_size][num_kv_heads][head_dim/2] */
+  const uint8_t* v_cache;
+  const uint8_t* k_sf;    /* [num_pages][page_size][num_kv_heads][head_dim/16] */
+  const uint8_t* v_sf;
+  const float* k_scale;   /* device fp32 scalar */
+  const float* v_scale;   /* device fp32 scalar */
+  int64_t num_pages;
+  int32_t page_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+} nvfp4kv_cache;
+
+/* Host-side launch plan of one prefill batch (filled by nvfp4_prefill_plan). */
+typedef struct {
+  int32_t batch, num_q_heads, num_kv_heads, head_dim, page_size;
+  int32_t max_q_len, max_kv_len;   /* [PR #5043] prefill plan() max lengths */
+  int64_t total_q, total_kv;
+  int32_t uniform_q;   /* [PR #3575] review: total_q == batch * max_q_len */
+  int32_t uniform_kv;  /* total_kv == batch * max_kv_len (informational) */
+  int32_t head_first;  /* [PR #3575] L2 gate: all KV streams fit in L2 */
+  int32_t block_q;     /* query tokens per tile (tile = block_q tokens x G heads) */
+  int32_t block_n;     /* keys per KV tile */
+  int32_t q_tiles_per_head; /* uniform: ceil(max_q_len / block_q) */
+  int32_t max_tile_cost;    /* KV tiles visited by the heaviest Q tile */
+  int32_t num_xcd;          /* XCDs the tile order is spread over */
+  int64_t num_tiles;        /* Q tiles over all requests and KV heads */
+  int64_t kv_bytes;         /* NVFP4 K+V bytes the batch reads */
+  int64_t l2_bytes;         /* L2 capacity used by the gate (all XCDs) */
+  int64_t workspace_bytes;  /* device workspace paged_prefill_causal needs */
+} nvfp4kv_prefill_plan;
+
+/*
+ * nvfp4_prefill_plan -- host-only plan step ([PR #5043] prefill plan();
+ * [PR #3575] uniform check and L2 gate).  Reads two host arrays with single
+ * vectorisable passes (no per-request work beyond one loop), touches no
+ * device memory.
+ *   qo_indptr_host  int32 [batch+1]: query rows of request r are
+ *                   [qo_indptr[r], qo_indptr[r+1]); qo_indptr[0] == 0.
+ *   kv_lens_host    int32 [batch]: cached keys of request r.  Lengths held
+ *                   as uint32 must be converted to int32 first.
+ *   kv_indptr_host  int32 [batch+1] or NULL: if given, each request must own
+ *                   exactly ceil(kv_len / page_size) page-table entries.
+ *   l2_bytes        L2 capacity of the whole device for the gate; 0 = query
+ *                   the current HIP device.
+ * Returns NVFP4KV_ERANGE if some q_len > kv_len, a length is negative, or a
+ * page count does not match; NVFP4KV_EUNSUPPORTED if head_dim is not 64 or
+ * 128, or num_q_heads / num_kv_heads is not 1, 2, 4 or 8.
+ */
+int nvfp4_prefill_plan(const int32_t* qo_indptr_host, const int32_t* kv_lens_host,
+                       const int32_t* kv_indptr_host, int32_t batch, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                       int64_t l2_bytes, nvfp4kv_prefill_plan* plan);
+
+/*
+ * paged_prefill_causal -- batched causal prefill attention over the NVFP4
+ * paged cache ([PR #4769]: each KV tile is dequantized once into a bf16 LDS
+ * staging tile outside the matrix-core loop; [PR #3575]: O(1) tile decode for
+ * uniform batches, heaviest-first Q tiles, L2-gated order).
+ *   q          bf16 [total_q][num_q_heads][head_dim], contiguous, 16-byte aligned.
+ *   qo_indptr  int32 [batch+1] (device copy of the plan's host array).
+ *   kv_indptr  int32 [batch+1]: request r's pages are
+ *              page_table[kv_indptr[r] .. kv_indptr[r+1]).
+ *   page_table int32 page ids; key j of request r is row
+ *              (page_table[kv_indptr[r] + j/page_size], j % page_size).
+ *   kv_lens    int32 [batch] (device copy of the plan's host array).
+ *   caches     host pointer to the cache descriptor (its pointers are device
+ *              pointers); geometry must match the plan.
+ *   out        bf16 [total_q][num_q_heads][head_dim].
+ *   sm_scale   softmax scale applied to q.k.
+ *   plan       host pointer, from nvfp4_prefill_plan for these lengths.
+ *   workspace  device buffer of at least plan->workspace_bytes (may be NULL
+ *              when that is 0), 256-byte aligned.
+ * Semantics: query row i of request r (q_len = Lq, kv_len = Lk) sits at
+ * position Lk - Lq + i and attends to keys 0 .. Lk - Lq + i (bottom-right
+ * causal alignment); query head h reads KV head h / (num_q_heads /
+ * num_kv_heads); o = softmax(sm_scale * q . k_hat) . v_hat with k_hat, v_hat
+ * the dequantized cache values.  Output rounded to bf16 (nearest-even).
+ * Page ids outside [0, num_pages) set NVFP4KV_DEV_PAGE_OOB and read as 0.
+ */
+int paged_prefill_causal(const void* q, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                         const int32_t* page_table, const int32_t* kv_lens,
+                         const nvfp4kv_cache* caches, void* out, float sm_scale,
+                         const nvfp4kv_prefill_plan* plan, void* workspace,
+                         int64_t workspace_bytes, uint32_t* dev_error, void* stream);
+
+/*
+ * nvfp4kv_read_device_error -- the one synchronizing call: waits for `stream`,
+ * copies the device error word to *bits_host and, if clear != 0, resets it to
+ * 0.  Not for use under graph capture.
+ */
+int nvfp4kv_read_device_error(uint32_t* dev_error, void* stream, uint32_t* bits_host, int clear);
+
+/* Human-readable name of a status code (static storage). */
+const char* nvfp4kv_status_string(int status);
+
+/* ABI version of this header (major * 100 + minor). */
+int nvfp4kv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4KV_H */

@@ -1,0 +1,333 @@
+"""Python binding of the MI355X NVFP4 paged-KV library (libnvfp4kv.so).
+
+Argument marshalling only: every step of the append and of the prefill runs
+in the library's HIP kernels.  torch supplies device memory and the current
+stream.  Importing this package does not need a GPU; calling the device
+entry points does, and they raise if the built library is missing.
+
+Entry points (same names as the C ABI in include/nvfp4kv.h):
+  nvfp4_append_paged_kv(k, v, slot_mapping, k_scale, v_scale,
+                        k_cache, v_cache, k_sf, v_sf, page_size)
+  plan(qo_indptr, kv_lens, num_q_heads, num_kv_heads, head_dim, page_size)
+  paged_prefill_causal(q, qo_indptr, kv_indptr, page_table, kv_lens, caches,
+                       out, sm_scale, plan=None)
+  read_device_error(device=None, clear=True)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional, Union
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnvfp4kv.so")
+
+OK, EINVAL, EUNSUPPORTED, ERANGE, EHIP, EWORKSPACE = 0, -1, -2, -3, -4, -5
+DEV_BAD_K_SCALE, DEV_BAD_V_SCALE, DEV_SLOT_OOB, DEV_PAGE_OOB, DEV_BAD_SCALE_ATTN = 1, 2, 4, 8, 16
+
+ENTRY_POINTS = ("nvfp4_append_paged_kv", "nvfp4_prefill_plan", "paged_prefill_causal",
+                "nvfp4kv_read_device_error", "nvfp4kv_status_string", "nvfp4kv_abi_version")
+
+
+class NVFP4KVError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {lib().nvfp4kv_status_string(status).decode()} (status {status})")
+
+
+class Cache(ctypes.Structure):
+    _fields_ = [("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+                ("k_sf", ctypes.c_void_p), ("v_sf", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("num_pages", ctypes.c_int64), ("page_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+
+
+class PlanStruct(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("batch", "num_q_heads", "num_kv_heads", "head_dim", "page_size",
+                 "max_q_len", "max_kv_len")] + \
+               [("total_q", ctypes.c_int64), ("total_kv", ctypes.c_int64)] + \
+               [(n, ctypes.c_int32) for n in
+                ("uniform_q", "uniform_kv", "head_first", "block_q", "block_n",
+                 "q_tiles_per_head", "max_tile_cost", "num_xcd")] + \
+               [(n, ctypes.c_int64) for n in
+                ("num_tiles", "kv_bytes", "l2_bytes", "workspace_bytes")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+_lib = None
+
+
+def lib():
+    """The loaded C library.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        path = os.environ.get("NVFP4KV_LIBRARY", LIB_PATH)
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
+                               "`python nvfp4_paged_kv_amd/build.py` (hipcc, gfx950)")
+        L = ctypes.CDLL(path)
+        P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        L.nvfp4_append_paged_kv.argtypes = [P, P, P, I64, P, P, P, P, P, P, I64, I32, I32, I32, P, P]
+        L.nvfp4_append_paged_kv.restype = ctypes.c_int
+        L.nvfp4_prefill_plan.argtypes = [P, P, P, I32, I32, I32, I32, I32, I64,
+                                         ctypes.POINTER(PlanStruct)]
+        L.nvfp4_prefill_plan.restype = ctypes.c_int
+        L.paged_prefill_causal.argtypes = [P, P, P, P, P, ctypes.POINTER(Cache), P, ctypes.c_float,
+                                           ctypes.POINTER(PlanStruct), P, I64, P, P]
+        L.paged_prefill_causal.restype = ctypes.c_int
+        L.nvfp4kv_read_device_error.argtypes = [P, P, ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]
+        L.nvfp4kv_read_device_error.restype = ctypes.c_int
+        L.nvfp4kv_status_string.argtypes = [ctypes.c_int]
+        L.nvfp4kv_status_string.restype = ctypes.c_char_p
+        L.nvfp4kv_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status == EINVAL or status == ERANGE:
+        raise ValueError(f"{what}: {lib().nvfp4kv_status_string(status).decode()}")
+    if status != OK:
+        raise NVFP4KVError(status, what)
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+# one device error word per device (int32 zeros; a torch fill, not a copy)
+_err_words: dict = {}
+
+
+def _norm_device(device) -> torch.device:
+    device = torch.device(device)
+    if device.type == "cuda" and device.index is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    return device
+
+
+def device_error_word(device) -> torch.Tensor:
+    """The library's default device error word for `device` (one per device)."""
+    device = _norm_device(device)
+    if device not in _err_words:
+        _err_words[device] = torch.zeros(1, dtype=torch.int32, device=device)
+    return _err_words[device]
+
+
+def read_device_error(device=None, clear: bool = True, word: Optional[torch.Tensor] = None) -> int:
+    """Synchronizing read of the device error bits (the only syncing call)."""
+    if word is None:
+        word = device_error_word(device if device is not None else "cuda")
+    bits = ctypes.c_uint32(0)
+    _check(lib().nvfp4kv_read_device_error(ctypes.c_void_p(word.data_ptr()), _stream(word.device),
+                                           ctypes.byref(bits), int(clear)), "read_device_error")
+    return int(bits.value)
+
+
+def _scale_tensor(name: str, value, device: torch.device) -> torch.Tensor:
+    """Global decode scale as a device fp32 scalar, following the FlashInfer
+    PR #6204 page's scale contract: a float or CPU tensor is checked on the host
+    (ValueError); a device tensor is left to the kernel's own check, because
+    reading it here would synchronize the host with the stream."""
+    if isinstance(value, torch.Tensor) and value.device.type == "cuda":
+        if value.numel() != 1 or value.dtype != torch.float32:
+            raise ValueError(f"{name} must be a scalar torch.float32 tensor")
+        if value.device != device:
+            raise ValueError(f"{name} must be on {device}")
+        if not value.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        return value
+    if isinstance(value, torch.Tensor):
+        if value.numel() != 1:
+            raise ValueError(f"{name} must be a scalar")
+        value = float(value.reshape(()).item())
+    value = float(value)
+    if not math.isfinite(value) or value <= 0.0:
+        raise ValueError(f"{name} must be a positive finite global decode scale")
+    return torch.full((), value, dtype=torch.float32, device=device)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+
+
+def nvfp4_append_paged_kv(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, k_scale,
+                          v_scale, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          k_sf: torch.Tensor, v_sf: torch.Tensor, page_size: int,
+                          dev_error: Optional[torch.Tensor] = None):
+    """Quantize k/v (bf16 [T, H_kv, D]) to NVFP4 and write them at slot_mapping
+    (int64 [T]) into the NHD caches (uint8 [P, page_size, H_kv, D/2]) and
+    scale-factor pages (uint8 [P, page_size, H_kv, D/16]).  Never synchronizes."""
+    if k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("k and v must be [num_tokens, num_kv_heads, head_dim] of equal shape")
+    T, H, D = k.shape
+    dev = k.device
+    for name, t, dt in (("k", k, torch.bfloat16), ("v", v, torch.bfloat16),
+                        ("slot_mapping", slot_mapping, torch.int64), ("k_cache", k_cache, torch.uint8),
+                        ("v_cache", v_cache, torch.uint8), ("k_sf", k_sf, torch.uint8),
+                        ("v_sf", v_sf, torch.uint8)):
+        if t.dtype != dt:
+            raise ValueError(f"{name} must be {dt}")
+        if t.device != dev:
+            raise ValueError(f"{name} must be on {dev}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    P = k_cache.shape[0]
+    if k_cache.shape != (P, page_size, H, D // 2) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must be [num_pages, page_size, num_kv_heads, head_dim/2]")
+    if k_sf.shape != (P, page_size, H, D // 16) or v_sf.shape != k_sf.shape:
+        raise ValueError("k_sf/v_sf must be [num_pages, page_size, num_kv_heads, head_dim/16]")
+    ks = _scale_tensor("k_scale", k_scale, dev)
+    vs = _scale_tensor("v_scale", v_scale, dev)
+    err = dev_error if dev_error is not None else device_error_word(dev)
+    _check(lib().nvfp4_append_paged_kv(
+        _ptr(k), _ptr(v), _ptr(slot_mapping), T, _ptr(ks), _ptr(vs), _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_sf), _ptr(v_sf), P, page_size, H, D, _ptr(err), _stream(dev)), "nvfp4_append_paged_kv")
+
+
+@dataclass
+class PagedCache:
+    """An NVFP4 paged KV cache (NHD pages) with its global decode scales."""
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    k_sf: torch.Tensor
+    v_sf: torch.Tensor
+    k_scale: torch.Tensor
+    v_scale: torch.Tensor
+
+    @classmethod
+    def empty(cls, num_pages, page_size, num_kv_heads, head_dim, device, k_scale=1.0, v_scale=1.0,
+              fill: Optional[int] = 0):
+        def mk(last):
+            t = torch.empty((num_pages, page_size, num_kv_heads, last), dtype=torch.uint8, device=device)
+            if fill is not None:
+                t.fill_(fill)
+            return t
+        return cls(mk(head_dim // 2), mk(head_dim // 2), mk(head_dim // 16), mk(head_dim // 16),
+                   _scale_tensor("k_scale", k_scale, torch.device(device)),
+                   _scale_tensor("v_scale", v_scale, torch.device(device)))
+
+    @property
+    def num_pages(self):
+        return self.k_cache.shape[0]
+
+    @property
+    def page_size(self):
+        return self.k_cache.shape[1]
+
+    @property
+    def num_kv_heads(self):
+        return self.k_cache.shape[2]
+
+    @property
+    def head_dim(self):
+        return self.k_cache.shape[3] * 2
+
+    def append(self, k, v, slot_mapping, dev_error=None):
+        nvfp4_append_paged_kv(k, v, slot_mapping, self.k_scale, self.v_scale, self.k_cache,
+                              self.v_cache, self.k_sf, self.v_sf, self.page_size, dev_error)
+
+    def _struct(self) -> Cache:
+        return Cache(self.k_cache.data_ptr(), self.v_cache.data_ptr(), self.k_sf.data_ptr(),
+                     self.v_sf.data_ptr(), self.k_scale.data_ptr(), self.v_scale.data_ptr(),
+                     self.num_pages, self.page_size, self.num_kv_heads, self.head_dim)
+
+
+class Plan:
+    """Host-side plan of one prefill batch (FlashInfer PR #5043 page: plan()
+    max lengths from tensor reductions, lengths cast to int32 at entry)."""
+
+    def __init__(self, qo_indptr, kv_lens, num_q_heads, num_kv_heads, head_dim, page_size,
+                 kv_indptr=None, l2_bytes: int = 0):
+        qo = _host_int32(qo_indptr, "qo_indptr")
+        kvl = _host_int32(kv_lens, "kv_lens")
+        kvp = _host_int32(kv_indptr, "kv_indptr") if kv_indptr is not None else None
+        if qo.numel() != kvl.numel() + 1:
+            raise ValueError("qo_indptr must have batch + 1 entries")
+        self.struct = PlanStruct()
+        _check(lib().nvfp4_prefill_plan(
+            _ptr(qo), _ptr(kvl), _ptr(kvp), kvl.numel(), num_q_heads, num_kv_heads, head_dim,
+            page_size, l2_bytes, ctypes.byref(self.struct)), "nvfp4_prefill_plan")
+        self.qo_host, self.kv_lens_host = qo, kvl
+        self._workspace = {}
+
+    def __getattr__(self, name):
+        if name == "struct":
+            raise AttributeError(name)
+        return getattr(self.struct, name)
+
+    def workspace(self, device) -> Optional[torch.Tensor]:
+        n = self.struct.workspace_bytes
+        if n == 0:
+            return None
+        device = torch.device(device)
+        if device not in self._workspace:
+            self._workspace[device] = torch.empty(n, dtype=torch.uint8, device=device)
+        return self._workspace[device]
+
+
+def _host_int32(t, name) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        t = torch.as_tensor(t)
+    if t.device.type != "cpu":
+        raise ValueError(f"{name} must be a host (CPU) tensor for the plan step")
+    t = t.flatten()
+    if t.dtype == torch.uint32:
+        t = t.to(torch.int64)
+    return t.to(torch.int32).contiguous()
+
+
+def plan(qo_indptr, kv_lens, num_q_heads, num_kv_heads, head_dim, page_size, kv_indptr=None,
+         l2_bytes: int = 0) -> Plan:
+    return Plan(qo_indptr, kv_lens, num_q_heads, num_kv_heads, head_dim, page_size, kv_indptr,
+                l2_bytes)
+
+
+def paged_prefill_causal(q: torch.Tensor, qo_indptr: torch.Tensor, kv_indptr: torch.Tensor,
+                         page_table: torch.Tensor, kv_lens: torch.Tensor, caches: PagedCache,
+                         out: torch.Tensor, sm_scale: float, plan: Optional[Plan] = None,
+                         dev_error: Optional[torch.Tensor] = None):
+    """Causal prefill over the NVFP4 paged cache.  q/out: bf16 [total_q, H_q, D];
+    qo_indptr, kv_indptr, page_table, kv_lens: int32 device tensors.  Without
+    `plan`, qo_indptr and kv_lens may instead be host tensors (the plan is then
+    computed here and the arrays are uploaded)."""
+    dev = q.device
+    if plan is None:
+        plan = Plan(qo_indptr.cpu() if qo_indptr.device.type == "cpu" else _need_host("qo_indptr"),
+                    kv_lens.cpu() if kv_lens.device.type == "cpu" else _need_host("kv_lens"),
+                    q.shape[1], caches.num_kv_heads, caches.head_dim, caches.page_size)
+    if qo_indptr.device.type == "cpu":
+        qo_indptr = qo_indptr.to(torch.int32).pin_memory().to(dev, non_blocking=True)
+    if kv_lens.device.type == "cpu":
+        kv_lens = kv_lens.to(torch.int32).pin_memory().to(dev, non_blocking=True)
+    for name, t, dt in (("q", q, torch.bfloat16), ("out", out, torch.bfloat16),
+                        ("qo_indptr", qo_indptr, torch.int32), ("kv_indptr", kv_indptr, torch.int32),
+                        ("page_table", page_table, torch.int32), ("kv_lens", kv_lens, torch.int32)):
+        if t.dtype != dt or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor on {dev}")
+    if q.dim() != 3 or out.shape != q.shape or q.shape[2] != caches.head_dim:
+        raise ValueError("q/out must be [total_q, num_q_heads, head_dim]")
+    if q.shape[0] != plan.total_q or q.shape[1] != plan.num_q_heads:
+        raise ValueError("q does not match the plan")
+    ws = plan.workspace(dev)
+    err = dev_error if dev_error is not None else device_error_word(dev)
+    cs = caches._struct()
+    _check(lib().paged_prefill_causal(
+        _ptr(q), _ptr(qo_indptr), _ptr(kv_indptr), _ptr(page_table), _ptr(kv_lens), ctypes.byref(cs),
+        _ptr(out), float(sm_scale), ctypes.byref(plan.struct), _ptr(ws),
+        0 if ws is None else ws.numel(), _ptr(err), _stream(dev)), "paged_prefill_causal")
+    return out
+
+
+def _need_host(name):
+    raise ValueError(f"{name} must be a host tensor when no plan is given")

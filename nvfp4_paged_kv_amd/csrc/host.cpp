@@ -1,0 +1,141 @@
+// host.cpp -- host side of the C ABI: the prefill plan, status strings, the
+// synchronizing device-error read and the device property cache.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <vector>
+
+#include "nvfp4kv_internal.hpp"
+
+namespace nvfp4kv {
+
+const DeviceProps& device_props() {
+  static std::mutex mu;
+  static std::vector<DeviceProps> cache;
+  static std::vector<bool> have;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cache.size() <= dev) {
+    cache.resize(dev + 1);
+    have.resize(dev + 1, false);
+  }
+  if (!have[dev]) {
+    DeviceProps p{256, 8, 4 << 20};
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      p.cu_count = v;
+    // gfx950 groups 32 CUs per XCD; each XCD has its own L2.
+    p.num_xcd = p.cu_count >= 32 ? p.cu_count / 32 : 1;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeL2CacheSize, dev) == hipSuccess && v > 0)
+      p.l2_bytes_per_xcd = v;
+    cache[dev] = p;
+    have[dev] = true;
+  }
+  return cache[dev];
+}
+
+}  // namespace nvfp4kv
+
+using namespace nvfp4kv;
+
+extern "C" int nvfp4_prefill_plan(const int32_t* qo_indptr_host, const int32_t* kv_lens_host,
+                                  const int32_t* kv_indptr_host, int32_t batch,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t page_size, int64_t l2_bytes,
+                                  nvfp4kv_prefill_plan* plan) {
+  if (!plan || batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || page_size <= 0 ||
+      head_dim <= 0 || (batch > 0 && (!qo_indptr_host || !kv_lens_host)))
+    return NVFP4KV_EINVAL;
+  if (num_q_heads % num_kv_heads != 0) return NVFP4KV_EUNSUPPORTED;
+  const int G = num_q_heads / num_kv_heads;
+  if (!(G == 1 || G == 2 || G == 4 || G == 8)) return NVFP4KV_EUNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return NVFP4KV_EUNSUPPORTED;
+  if (batch > 0 && qo_indptr_host[0] != 0) return NVFP4KV_ERANGE;
+
+  nvfp4kv_prefill_plan p{};
+  p.batch = batch;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.page_size = page_size;
+  p.block_q = kTileRows / G;
+  p.block_n = kBlockN;
+  // One pass of reductions over the host arrays ([PR #5043]: max lengths from
+  // a vectorised reduction, not a per-request Python loop).
+  int32_t max_q = 0, max_kv = 0;
+  int64_t tot_q = 0, tot_kv = 0, qtiles = 0;
+  int32_t max_cost = 0;
+  bool bad = false;
+  for (int32_t r = 0; r < batch; ++r) {
+    const int32_t lq = qo_indptr_host[r + 1] - qo_indptr_host[r];
+    const int32_t lk = kv_lens_host[r];
+    bad |= (lq < 0) | (lk < 0) | (lq > lk);
+    if (kv_indptr_host)
+      bad |= (kv_indptr_host[r + 1] - kv_indptr_host[r]) != (lk + page_size - 1) / page_size;
+    max_q = lq > max_q ? lq : max_q;
+    max_kv = lk > max_kv ? lk : max_kv;
+    tot_q += lq;
+    tot_kv += lk;
+    qtiles += (lq + p.block_q - 1) / p.block_q;
+    // heaviest tile of this request: its last one, whose last row sees keys 0..lk-1
+    const int32_t cost = lq > 0 ? (lk - 1) / kBlockN + 1 : 0;
+    max_cost = cost > max_cost ? cost : max_cost;
+  }
+  if (bad) return NVFP4KV_ERANGE;
+  if (kv_indptr_host && batch > 0 && kv_indptr_host[0] != 0) return NVFP4KV_ERANGE;
+  p.max_q_len = max_q;
+  p.max_kv_len = max_kv;
+  p.total_q = tot_q;
+  p.total_kv = tot_kv;
+  p.uniform_q = tot_q == (int64_t)batch * max_q;  // [PR #3575] review: O(1) uniform check
+  p.uniform_kv = tot_kv == (int64_t)batch * max_kv;
+  p.q_tiles_per_head = (max_q + p.block_q - 1) / p.block_q;
+  p.max_tile_cost = max_cost;
+  p.num_tiles = qtiles * num_kv_heads;
+  // [PR #3575] L2 gate: KV bytes = tokens x heads x bytes per token-head (K and
+  // V, NVFP4: head_dim/2 code bytes + head_dim/16 scale bytes each); the
+  // head-first (global reverse) order only when twice that fits in L2.
+  p.kv_bytes = tot_kv * num_kv_heads * (int64_t)(head_dim / 2 + head_dim / 16) * 2;
+  if (l2_bytes > 0) {
+    p.l2_bytes = l2_bytes;
+    p.num_xcd = 8;
+  } else {
+    const DeviceProps& d = device_props();
+    p.l2_bytes = d.l2_bytes_per_xcd * d.num_xcd;
+    p.num_xcd = d.num_xcd;
+  }
+  p.head_first = 2 * p.kv_bytes <= p.l2_bytes;
+  // Ragged batches need a device work list: 2 int32 per tile, plus counters.
+  p.workspace_bytes = p.uniform_q ? 0 : (int64_t)(p.num_tiles * 8 + 4096 + 255) / 256 * 256;
+  *plan = p;
+  return NVFP4KV_OK;
+}
+
+extern "C" int nvfp4kv_read_device_error(uint32_t* dev_error, void* stream, uint32_t* bits_host,
+                                         int clear) {
+  if (!dev_error || !bits_host) return NVFP4KV_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  if (hipMemcpyAsync(bits_host, dev_error, 4, hipMemcpyDeviceToHost, s) != hipSuccess)
+    return NVFP4KV_EHIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return NVFP4KV_EHIP;
+  if (clear) {
+    if (hipMemsetAsync(dev_error, 0, 4, s) != hipSuccess) return NVFP4KV_EHIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return NVFP4KV_EHIP;
+  }
+  return NVFP4KV_OK;
+}
+
+extern "C" const char* nvfp4kv_status_string(int status) {
+  switch (status) {
+    case NVFP4KV_OK: return "ok";
+    case NVFP4KV_EINVAL: return "invalid argument (null pointer, size or alignment)";
+    case NVFP4KV_EUNSUPPORTED: return "unsupported shape (head_dim or GQA group size)";
+    case NVFP4KV_ERANGE: return "inconsistent lengths (q_len > kv_len, negative length or page count)";
+    case NVFP4KV_EHIP: return "HIP runtime error";
+    case NVFP4KV_EWORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int nvfp4kv_abi_version(void) { return 100; }

@@ -1,0 +1,455 @@
+// prefill.hip -- batched causal prefill attention over the NVFP4 paged KV
+// cache (gfx950, wave64, bf16 MFMA).
+//
+// Design points taken from the pages, re-made for CDNA4:
+//  * FlashInfer PR #4769 page (NVFP4 KV tile repack; code analysis and "why"
+//    sections): decoding NVFP4 inside the matrix-multiply loop made the
+//    kernel instruction-bound; each KV tile is instead dequantized ONCE into a
+//    16-bit staging tile that the matrix cores then read natively.  Here: the
+//    whole workgroup decodes the tile (E2M1 x E4M3 is exact in bf16) into LDS;
+//    K is staged [key][d], V transposed [d][key] so both feed
+//    v_mfma_f32_32x32x16_bf16 with 16-byte LDS reads.  The global scales are
+//    not applied in the staging tile: g_k folds into the softmax scale and
+//    g_v into the epilogue.
+//  * FlashInfer PR #3575 page (FP8 causal attention): section 1, O(1) tile
+//    decode when every request has the same query length (uniform flag from
+//    the plan); section 2, the heaviest causal Q tiles of all requests and
+//    heads are issued first; section 3, that global order only when the KV
+//    working set fits in L2 (here the sum of the 8 XCD L2s; tiles of one
+//    (request, KV head) stream stay on one XCD).  Ragged batches use a work
+//    list sorted by tile cost on the device.
+//
+// Tile = 128 query rows: block_q = 128/G consecutive tokens x the G query
+// heads sharing one KV head (GQA packing).  4 waves x 32 rows.  KV tile = 64
+// keys.  The score tile is computed transposed, S^T = K Q^T, so every lane
+// owns one query row (lane % 32) and its softmax state stays in registers;
+// O^T = V^T P^T then keeps the same row per lane, and P^T comes straight out
+// of the S^T accumulators without any data movement.
+#include <hip/hip_runtime.h>
+
+#include "nvfp4kv_codec.hpp"
+#include "nvfp4kv_internal.hpp"
+
+namespace nvfp4kv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+struct PrefillArgs {
+  const uint16_t* q;
+  const int32_t* qo;
+  const int32_t* kvp;
+  const int32_t* pt;
+  const int32_t* kvl;
+  const uint8_t* kc;
+  const uint8_t* vc;
+  const uint8_t* ksf;
+  const uint8_t* vsf;
+  const float* kscale;
+  const float* vscale;
+  uint16_t* out;
+  const int2* worklist;  // ragged batches; null when uniform
+  uint32_t* err;
+  int64_t num_pages;
+  FastDiv ps_div;
+  int Hq, Hk;
+  float sm_scale_log2;  // sm_scale * log2(e)
+  int B, QT, head_first, nxcd;
+  uint32_t num_tiles;
+};
+
+template <int D, int G>
+struct Cfg {
+  static constexpr int BQ = kTileRows / G;  // query tokens per tile
+  static constexpr int BN = kBlockN;        // keys per KV tile
+  static constexpr int KROW = D * 2;        // bytes of one staged K row
+  static constexpr int KCH = D / 8;         // 16-byte chunks per K row
+  static constexpr int VROW = BN * 2;       // bytes of one staged V^T row
+  static constexpr int K_LDS = BN * KROW;
+  static constexpr int V_LDS = D * VROW;
+  static constexpr int NDC = D / 16;        // MFMA k-steps over head_dim
+  static constexpr int NDB = D / 32;        // 32-wide head_dim blocks of O^T
+  static constexpr int JOBS = 4 * D;        // 32-element dequant jobs per KV tile (K and V)
+};
+
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  // lo, hi are exactly representable in bf16: keep their upper halves.
+  return __builtin_amdgcn_perm(f2u(hi), f2u(lo), 0x07060302u);
+}
+
+// Position of key x (0..63) inside a staged V^T row: within each 16-key group
+// bits 2 and 3 are swapped so that lane half h of the P^T operand (keys
+// 4h..4h+3 and 8+4h..8+4h+3 of the group) reads 8 contiguous positions.
+__device__ __forceinline__ int vpos(int x) {
+  return (x & ~15) | (x & 3) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+// XOR swizzles of the 16-byte chunk index (bank-conflict avoidance).
+template <int D>
+__device__ __forceinline__ int kswz(int key) { return key & (D / 8 - 1); }
+__device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+  using C = Cfg<D, G>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::K_LDS + C::V_LDS];
+  uint8_t* const sK = smem;
+  uint8_t* const sV = smem + C::K_LDS;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, hh = lane >> 5;
+
+  // ---- which (request, KV head, Q tile) this workgroup computes
+  int b, hk, qt;
+  const uint32_t tile = blockIdx.x;
+  if (a.worklist) {
+    const int2 e = a.worklist[tile];
+    b = e.x;
+    qt = e.y / a.Hk;
+    hk = e.y - qt * a.Hk;
+  } else {
+    const uint32_t bh_n = (uint32_t)a.B * a.Hk;
+    uint32_t bh, qrev;
+    if (a.head_first) {
+      // heaviest Q tiles of every (request, head) first
+      qrev = tile / bh_n;
+      bh = tile - qrev * bh_n;
+    } else {
+      // stream-major: XCD x (blockIdx % nxcd) owns a contiguous range of
+      // (request, head) streams, each walked heaviest tile first
+      const uint32_t nx = a.nxcd, x = tile % nx, s = tile / nx;
+      const uint32_t per = a.num_tiles / nx, rem = a.num_tiles % nx;
+      const uint32_t L = x * per + (x < rem ? x : rem) + s;
+      bh = L / a.QT;
+      qrev = L - bh * a.QT;
+    }
+    b = bh / a.Hk;
+    hk = bh - b * a.Hk;
+    qt = a.QT - 1 - qrev;
+  }
+
+  const int q_begin = a.qo[b];
+  const int Lq = a.qo[b + 1] - q_begin;
+  const int Lk = a.kvl[b];
+  const int off = Lk - Lq;  // bottom-right causal alignment
+  const int q0 = qt * C::BQ;
+  const int rows_valid = min(C::BQ, Lq - q0);
+  if (rows_valid <= 0) return;  // (uniform batches with short requests)
+  const int kend_max = off + q0 + rows_valid - 1;  // last key any row sees
+  const int kend_min = off + q0;                   // last key of the first row
+  const int ntiles = kend_max / C::BN + 1;
+
+  const int r = wave * 32 + n;  // this lane's tile row
+  const int tr = r % C::BQ, g = r / C::BQ;
+  const bool row_valid = tr < rows_valid;
+  const int tok = q0 + tr;
+  const int hq = hk * G + g;
+  const int kend = off + tok;
+
+  const float gk = *a.kscale, gv = *a.vscale;
+  if (tile == 0 && tid == 0 && !(scale_ok(gk) && scale_ok(gv)))
+    atomicOr(a.err, (uint32_t)NVFP4KV_DEV_BAD_SCALE_ATTN);
+  const float cscale = a.sm_scale_log2 * gk;
+
+  // ---- Q^T operand fragments: lane holds Q[row][16c + 8hh .. +7]
+  bf16x8 qf[C::NDC];
+  {
+    const uint16_t* qrow = a.q + ((int64_t)(q_begin + (row_valid ? tok : q0)) * a.Hq + hq) * D;
+#pragma unroll
+    for (int c = 0; c < C::NDC; ++c) {
+      u32x4 w = row_valid ? *(const u32x4*)(qrow + c * 16 + hh * 8) : (u32x4){0, 0, 0, 0};
+      __builtin_memcpy(&qf[c], &w, 16);
+    }
+  }
+
+  f32x16 o[C::NDB];
+#pragma unroll
+  for (int i = 0; i < C::NDB; ++i) o[i] = (f32x16){};
+  float m_run = -__builtin_inff(), l_run = 0.0f;
+
+  const int32_t* ptb = a.pt + a.kvp[b];
+  const int ps = (int)a.ps_div.d;
+
+  for (int jt = 0; jt < ntiles; ++jt) {
+    __syncthreads();  // previous tile's LDS reads are done
+    // ---- dequantize the NVFP4 K and V tile into bf16 LDS staging (once)
+#pragma unroll
+    for (int job0 = 0; job0 < C::JOBS; job0 += 256) {
+      const int job = job0 + tid;
+      if (C::JOBS % 256 == 0 || job < C::JOBS) {
+        const int tensor = job / (2 * D);  // 0: K, 1: V
+        const int idx = job - tensor * 2 * D;
+        const int key = idx / (D / 32), part = idx % (D / 32);
+        const int kk = jt * C::BN + key;
+        u32x4 pk = {0, 0, 0, 0};
+        uint32_t sfw = 0;
+        if (kk <= kend_max) {  // later keys are masked for every row: zeros
+          const int pi = (int)fastdiv((uint32_t)kk, a.ps_div);
+          const int page = ptb[pi];
+          if ((uint32_t)page < (uint64_t)a.num_pages) {
+            const int64_t row = ((int64_t)page * ps + (kk - pi * ps)) * a.Hk + hk;
+            const uint8_t* cb = tensor ? a.vc : a.kc;
+            const uint8_t* sb = tensor ? a.vsf : a.ksf;
+            pk = *(const u32x4*)(cb + row * (D / 2) + part * 16);
+            sfw = *(const uint16_t*)(sb + row * (D / 16) + part * 2);
+          } else {
+            atomicOr(a.err, (uint32_t)NVFP4KV_DEV_PAGE_OOB);
+          }
+        }
+        const float S0 = e4m3_decode(sfw & 0xFFu), S1 = e4m3_decode(sfw >> 8);
+        uint32_t ow[16];  // 32 bf16 values, element 2i in the low half of ow[i]
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float S = w < 2 ? S0 : S1;
+          f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[w], 1.0f, 0);
+          f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[w], 1.0f, 1);
+          f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[w], 1.0f, 2);
+          f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[w], 1.0f, 3);
+          ow[4 * w + 0] = bf16_pair(f0[0] * S, f0[1] * S);
+          ow[4 * w + 1] = bf16_pair(f1[0] * S, f1[1] * S);
+          ow[4 * w + 2] = bf16_pair(f2[0] * S, f2[1] * S);
+          ow[4 * w + 3] = bf16_pair(f3[0] * S, f3[1] * S);
+        }
+        if (tensor == 0) {
+          uint8_t* rowp = sK + key * C::KROW;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int ch = (part * 4 + i) ^ kswz<D>(key);
+            *(u32x4*)(rowp + ch * 16) = (u32x4){ow[4 * i], ow[4 * i + 1], ow[4 * i + 2], ow[4 * i + 3]};
+          }
+        } else {
+          const int p = vpos(key);
+#pragma unroll
+          for (int e = 0; e < 32; ++e) {
+            const int d = part * 32 + e;
+            const int ch = (p >> 3) ^ vswz(d);
+            *(uint16_t*)(sV + d * C::VROW + ch * 16 + (p & 7) * 2) =
+                (uint16_t)(e & 1 ? ow[e >> 1] >> 16 : ow[e >> 1] & 0xFFFFu);
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T for 64 keys: lane holds S^T[key 32kb + 8(i/4) + 4hh + i%4][row n]
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = (f32x16){};
+      const int key = kb * 32 + n;
+#pragma unroll
+      for (int c = 0; c < C::NDC; ++c) {
+        const int ch = (2 * c + hh) ^ kswz<D>(key);
+        bf16x8 kf;
+        __builtin_memcpy(&kf, sK + key * C::KROW + ch * 16, 16);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kb], 0, 0, 0);
+      }
+    }
+
+    // ---- causal mask (diagonal tiles only) + online softmax in log2 domain
+    const bool diag = jt * C::BN + C::BN - 1 > kend_min;
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float x = s[kb][i] * cscale;
+        const int key = jt * C::BN + kb * 32 + 8 * (i / 4) + 4 * hh + (i % 4);
+        if (diag && key > kend) x = -__builtin_inff();
+        s[kb][i] = x;
+        mx = __builtin_fmaxf(mx, x);
+      }
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = __builtin_fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(s[kb][i] - m_new);
+        s[kb][i] = p;
+        lsum += p;
+      }
+    l_run = l_run * alpha + lsum;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
+
+    // ---- P^T operands straight from the accumulators (16-key chunks)
+    bf16x8 pf[4];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pf[kc][j] = (__bf16)s[kc >> 1][8 * (kc & 1) + j];
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const int d = db * 32 + n;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        const int ch = (2 * kc + hh) ^ vswz(d);
+        bf16x8 vf;
+        __builtin_memcpy(&vf, sV + d * C::VROW + ch * 16, 16);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], o[db], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- epilogue: O / l * g_v -> bf16; lane holds O^T[d][row n]
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = gv / l_tot;
+  if (row_valid) {
+    uint16_t* orow = a.out + ((int64_t)(q_begin + tok) * a.Hq + hq) * D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = db * 32 + 8 * i4 + 4 * hh;
+        __bf16 v0 = (__bf16)(o[db][4 * i4 + 0] * inv), v1 = (__bf16)(o[db][4 * i4 + 1] * inv);
+        __bf16 v2 = (__bf16)(o[db][4 * i4 + 2] * inv), v3 = (__bf16)(o[db][4 * i4 + 3] * inv);
+        uint16_t u0, u1, u2, u3;
+        __builtin_memcpy(&u0, &v0, 2);
+        __builtin_memcpy(&u1, &v1, 2);
+        __builtin_memcpy(&u2, &v2, 2);
+        __builtin_memcpy(&u3, &v3, 2);
+        *(uint2*)(orow + d) = make_uint2(u0 | ((uint32_t)u1 << 16), u2 | ((uint32_t)u3 << 16));
+      }
+  }
+}
+
+// ---- ragged batches: device-built work list, heaviest tile first.
+// One workgroup: histogram of tile costs (KV tiles a Q tile visits), an
+// exclusive scan in descending cost order, then each request places its
+// tiles (x KV heads) at the next free positions of its cost buckets.
+constexpr int kCostBuckets = 4096;
+
+__global__ __launch_bounds__(1024) void worklist_kernel(const int32_t* __restrict__ qo,
+                                                        const int32_t* __restrict__ kvl, int B,
+                                                        int Hk, int BQ, int2* __restrict__ list) {
+  __shared__ int hist[kCostBuckets];
+  __shared__ int warp_tot[16];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kCostBuckets; i += 1024) hist[i] = 0;
+  __syncthreads();
+  for (int rq = tid; rq < B; rq += 1024) {
+    const int lq = qo[rq + 1] - qo[rq], off = kvl[rq] - lq;
+    for (int t = 0; t * BQ < lq; ++t) {
+      const int last = off + min((t + 1) * BQ, lq) - 1;
+      const int c = min(last / kBlockN + 1, kCostBuckets - 1);
+      atomicAdd(&hist[c], Hk);
+    }
+  }
+  __syncthreads();
+  // exclusive scan over buckets in descending cost: pos[c] = sum_{c' > c} hist[c']
+  // each thread owns 4 consecutive descending buckets
+  const int per = kCostBuckets / 1024;
+  int vals[per];
+  int sum = 0;
+  for (int i = 0; i < per; ++i) {
+    vals[i] = hist[kCostBuckets - 1 - (tid * per + i)];
+    sum += vals[i];
+  }
+  // inclusive scan of `sum` across the 1024 threads (wave64 shuffles + LDS)
+  int incl = sum;
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(incl, o);
+    if ((tid & 63) >= o) incl += y;
+  }
+  if ((tid & 63) == 63) warp_tot[tid >> 6] = incl;
+  __syncthreads();
+  int wbase = 0;
+  for (int w = 0; w < (tid >> 6); ++w) wbase += warp_tot[w];
+  int run = wbase + incl - sum;
+  __syncthreads();
+  for (int i = 0; i < per; ++i) {
+    hist[kCostBuckets - 1 - (tid * per + i)] = run;
+    run += vals[i];
+  }
+  __syncthreads();
+  for (int rq = tid; rq < B; rq += 1024) {
+    const int lq = qo[rq + 1] - qo[rq], off = kvl[rq] - lq;
+    for (int t = 0; t * BQ < lq; ++t) {
+      const int last = off + min((t + 1) * BQ, lq) - 1;
+      const int c = min(last / kBlockN + 1, kCostBuckets - 1);
+      const int p = atomicAdd(&hist[c], Hk);
+      for (int h = 0; h < Hk; ++h) list[p + h] = make_int2(rq, t * Hk + h);
+    }
+  }
+}
+
+template <int D, int G>
+void launch_prefill(const PrefillArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((prefill_kernel<D, G>), dim3(a.num_tiles), dim3(256), 0, s, a);
+}
+
+}  // namespace
+}  // namespace nvfp4kv
+
+using namespace nvfp4kv;
+
+extern "C" int paged_prefill_causal(const void* q, const int32_t* qo_indptr,
+                                    const int32_t* kv_indptr, const int32_t* page_table,
+                                    const int32_t* kv_lens, const nvfp4kv_cache* caches, void* out,
+                                    float sm_scale, const nvfp4kv_prefill_plan* plan,
+                                    void* workspace, int64_t workspace_bytes, uint32_t* dev_error,
+                                    void* stream) {
+  if (!plan || !caches) return NVFP4KV_EINVAL;
+  const nvfp4kv_prefill_plan& p = *plan;
+  const nvfp4kv_cache& c = *caches;
+  if (p.num_kv_heads != c.num_kv_heads || p.head_dim != c.head_dim ||
+      p.page_size != c.page_size || p.num_q_heads % p.num_kv_heads != 0)
+    return NVFP4KV_EINVAL;
+  if (p.num_tiles == 0) return NVFP4KV_OK;
+  if (!q || !qo_indptr || !kv_indptr || !page_table || !kv_lens || !out || !dev_error ||
+      !c.k_cache || !c.v_cache || !c.k_sf || !c.v_sf || !c.k_scale || !c.v_scale)
+    return NVFP4KV_EINVAL;
+  if (!aligned(q, 16) || !aligned(out, 8) || !aligned(c.k_cache, 16) || !aligned(c.v_cache, 16) ||
+      !aligned(c.k_sf, 2) || !aligned(c.v_sf, 2))
+    return NVFP4KV_EINVAL;
+  if (p.num_tiles >= (1ll << 31) || p.batch <= 0) return NVFP4KV_EUNSUPPORTED;
+  if (p.workspace_bytes > 0 && (!workspace || workspace_bytes < p.workspace_bytes ||
+                                !aligned(workspace, 256)))
+    return NVFP4KV_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  PrefillArgs a{};
+  a.q = (const uint16_t*)q;
+  a.qo = qo_indptr;
+  a.kvp = kv_indptr;
+  a.pt = page_table;
+  a.kvl = kv_lens;
+  a.kc = c.k_cache;
+  a.vc = c.v_cache;
+  a.ksf = c.k_sf;
+  a.vsf = c.v_sf;
+  a.kscale = c.k_scale;
+  a.vscale = c.v_scale;
+  a.out = (uint16_t*)out;
+  a.err = dev_error;
+  a.num_pages = c.num_pages;
+  a.ps_div = make_fastdiv((uint32_t)c.page_size);
+  a.Hq = p.num_q_heads;
+  a.Hk = p.num_kv_heads;
+  a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  a.B = p.batch;
+  a.QT = p.q_tiles_per_head;
+  a.head_first = p.head_first;
+  a.nxcd = p.num_xcd > 0 ? p.num_xcd : 1;
+  a.num_tiles = (uint32_t)p.num_tiles;
+  if (!p.uniform_q) {
+    a.worklist = (const int2*)workspace;
+    hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(1024), 0, s, qo_indptr, kv_lens, p.batch,
+                       p.num_kv_heads, p.block_q, (int2*)workspace);
+  }
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int D = p.head_dim;
+#define NVFP4KV_CASE(DD, GG) \
+  if (D == DD && G == GG) launch_prefill<DD, GG>(a, s); else
+  NVFP4KV_CASE(128, 1) NVFP4KV_CASE(128, 2) NVFP4KV_CASE(128, 4) NVFP4KV_CASE(128, 8)
+  NVFP4KV_CASE(64, 1) NVFP4KV_CASE(64, 2) NVFP4KV_CASE(64, 4) NVFP4KV_CASE(64, 8)
+  return NVFP4KV_EUNSUPPORTED;
+#undef NVFP4KV_CASE
+  return hipGetLastError() == hipSuccess ? NVFP4KV_OK : NVFP4KV_EHIP;
+}

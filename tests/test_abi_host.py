@@ -1,0 +1,158 @@
+"""CPU-only checks of the HIP library's host side: the C ABI exports, the
+plan step (FlashInfer PR #5043 page tests: max lengths for int32 / uint32
+lengths across batch and page sizes; PR #3575 page: uniform flag and L2
+gate), and a host build of the kernels' codec helpers against the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.fixture(scope="module")
+def K():
+    import nvfp4_paged_kv_amd as K
+    K.lib()
+    return K
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "nvfp4kv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol(K):
+    names = _declared_functions()
+    assert set(names) == set(K.ENTRY_POINTS), names
+    L = ctypes.CDLL(K.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert K.lib().nvfp4kv_abi_version() == 100
+    assert K.lib().nvfp4kv_status_string(-3).startswith(b"inconsistent")
+
+
+def _plan(K, qo, kv, hq=32, hk=8, d=128, ps=16, **kw):
+    return K.plan(torch.as_tensor(qo), torch.as_tensor(kv), hq, hk, d, ps, l2_bytes=32 << 20, **kw)
+
+
+@pytest.mark.parametrize("dtype", [torch.int32, torch.uint32])
+@pytest.mark.parametrize("batch", [1, 7, 64, 1024])
+@pytest.mark.parametrize("page_size", [1, 16, 64])
+def test_plan_max_lens(K, dtype, batch, page_size):
+    g = torch.Generator().manual_seed(batch * 131 + page_size)
+    kv = torch.randint(1, 5000, (batch,), generator=g)
+    q = torch.minimum(kv, torch.randint(0, 700, (batch,), generator=g))
+    qo = torch.zeros(batch + 1, dtype=torch.int64)
+    qo[1:] = torch.cumsum(q, 0)
+    npg = (kv + page_size - 1) // page_size
+    kvp = torch.zeros(batch + 1, dtype=torch.int64)
+    kvp[1:] = torch.cumsum(npg, 0)
+    p = K.plan(qo.to(torch.int32), kv.to(dtype), 32, 8, 128, page_size, kv_indptr=kvp.to(torch.int32),
+               l2_bytes=32 << 20)
+    assert p.max_q_len == int((qo[1:] - qo[:-1]).max())
+    assert p.max_kv_len == int(kv.max())
+    assert p.total_q == int(q.sum()) and p.total_kv == int(kv.sum())
+    assert p.uniform_q == int(bool((q == q.max()).all()))
+    bq = 128 // 4
+    assert p.block_q == bq
+    assert p.num_tiles == 8 * int(((q + bq - 1) // bq).sum())
+    assert p.max_tile_cost == int(((kv - 1) // 64 + 1)[q > 0].max()) if (q > 0).any() else True
+    assert p.kv_bytes == int(kv.sum()) * 8 * (64 + 8) * 2
+    assert p.head_first == int(2 * p.kv_bytes <= (32 << 20))
+    assert (p.workspace_bytes == 0) == bool(p.uniform_q)
+
+
+def test_plan_uniform_flags_and_tiles(K):
+    p = _plan(K, [0, 1024, 2048], [1024, 1024])
+    assert p.uniform_q == 1 and p.uniform_kv == 1 and p.q_tiles_per_head == 32 and p.num_tiles == 2 * 8 * 32
+    p = _plan(K, [0, 2048], [2048])
+    assert p.head_first == 1 and p.num_tiles == 8 * 64
+    p = _plan(K, [0, 10, 20], [10, 30])
+    assert p.uniform_q == 1 and p.uniform_kv == 0
+    p = _plan(K, [0, 10, 25], [10, 30])
+    assert p.uniform_q == 0 and p.workspace_bytes >= p.num_tiles * 8
+    p = _plan(K, [0, 128, 256], [128, 128], hq=4, hk=2, d=64)
+    assert p.block_q == 64 and p.num_tiles == 8
+
+
+def test_plan_rejects_bad_lengths(K):
+    with pytest.raises(ValueError):
+        _plan(K, [0, 10], [9])                       # q_len > kv_len
+    with pytest.raises(ValueError):
+        _plan(K, [1, 10], [20])                      # qo_indptr[0] != 0
+    with pytest.raises(ValueError):
+        _plan(K, [0, 10], [20], kv_indptr=torch.tensor([0, 3], dtype=torch.int32))  # needs 2 pages
+    with pytest.raises(K.NVFP4KVError):
+        _plan(K, [0, 10], [20], d=96)
+    with pytest.raises(K.NVFP4KVError):
+        _plan(K, [0, 10], [20], hq=24, hk=8)
+    p = _plan(K, [0], [])
+    assert p.num_tiles == 0
+
+
+def test_plan_empty_requests(K):
+    p = _plan(K, [0, 0, 5], [7, 5])
+    assert p.max_q_len == 5 and p.total_q == 5 and p.num_tiles == 8 and p.uniform_q == 0
+
+
+@pytest.fixture(scope="module")
+def host_codec():
+    path = os.path.join(HERE, "libcodec_host.so")
+    if not os.path.exists(path):
+        from nvfp4_paged_kv_amd.build import build_test_helpers
+        build_test_helpers()
+    return ctypes.CDLL(path)
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def test_kernel_software_e2m1_matches_oracle(host_codec, oracle):
+    """Every fp32 pattern of magnitude below 8 (then a stride above) through the
+    kernels' software E2M1 encoder (host build) and the oracle."""
+    chunk = 1 << 26
+    for lo in list(range(0, 0x41000000, chunk)) + [0x41000000 + i * 0x1000000 for i in range(0x3E)]:
+        pats = np.arange(lo, lo + chunk if lo < 0x41000000 else lo + (1 << 20), dtype=np.uint32)
+        pats = pats[pats <= 0x7F800000]
+        for sign in (0, 0x80000000):
+            p = pats | np.uint32(sign)
+            got = np.empty(p.size, np.uint8)
+            host_codec.host_e2m1_sw(_p(p), ctypes.c_int64(p.size), _p(got))
+            assert np.array_equal(got, oracle.e2m1_encode(p.view(np.float32))), hex(lo)
+
+
+def test_kernel_e4m3_encode_decode_matches_oracle(host_codec, oracle):
+    top = 0x7F800000
+    rng = np.random.default_rng(0)
+    pats = np.concatenate([np.arange(0, 0x3C800000 + 4096, 64, dtype=np.uint32),
+                           np.arange(0x3A000000, 0x44000000, 3, dtype=np.uint32),
+                           rng.integers(0, top + 1, 2_000_000, dtype=np.uint64).astype(np.uint32)])
+    s = pats.view(np.float32)
+    got = np.empty(s.size, np.uint8)
+    host_codec.host_e4m3(_p(s), ctypes.c_int64(s.size), _p(got))
+    assert np.array_equal(got, oracle.e4m3_encode(s))
+    codes = np.arange(0x7F, dtype=np.uint8)
+    dec = np.empty(codes.size, np.float32)
+    host_codec.host_e4m3_decode(_p(codes), ctypes.c_int64(codes.size), _p(dec))
+    assert [float(x) for x in dec] == [oracle.e4m3_value(int(c)) for c in codes]
+    host_codec.host_scale_ok.restype = ctypes.c_int
+    host_codec.host_scale_ok.argtypes = [ctypes.c_float]
+    for g in [1.0, 1e-40, 3e38, 0.0, -0.0, -1.0, float("nan"), float("inf"), -float("inf")]:
+        assert bool(host_codec.host_scale_ok(g)) == oracle.scale_ok(g), g
+
+
+def test_fastdiv(host_codec):
+    rng = np.random.default_rng(1)
+    n = np.concatenate([np.arange(0, 5000, dtype=np.uint32), np.array([2**32 - 1, 2**31, 2**31 - 1], np.uint32),
+                        rng.integers(0, 2**32, 200_000, dtype=np.uint64).astype(np.uint32)])
+    q = np.empty_like(n)
+    for d in [1, 2, 3, 7, 8, 16, 17, 64, 100, 1000, 65535, 65536, 123457, 2**31 - 1]:
+        host_codec.host_fastdiv(_p(n), ctypes.c_int64(n.size), ctypes.c_uint32(d), _p(q))
+        assert np.array_equal(q, n // np.uint32(d)), d

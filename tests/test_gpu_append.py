@@ -1,0 +1,183 @@
+"""GPU parity of the NVFP4 append (bit-exact against the oracle) and its
+boundary behaviour: device scale checks (eager and graph replay), zero rows,
+padding / out-of-range slots, and no host synchronization."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_helpers import SENTINEL, banner
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    import nvfp4_paged_kv_amd as K
+    K.lib()
+    return K
+
+
+def _oracle_cache(O, k, v, slots, ks, vs, P, ps):
+    T, H, D = k.shape
+    c = [np.full((P, ps, H, D // 2), SENTINEL, np.uint8), np.full((P, ps, H, D // 2), SENTINEL, np.uint8),
+         np.full((P, ps, H, D // 16), SENTINEL, np.uint8), np.full((P, ps, H, D // 16), SENTINEL, np.uint8)]
+    err = O.append(W.bf16_bits(k), W.bf16_bits(v), slots.cpu().numpy(), ks, vs, *c, ps)
+    return c, err
+
+
+def _gpu_append(K, k, v, slots, ks, vs, P, ps, err_word=None):
+    T, H, D = k.shape
+    cache = K.PagedCache.empty(P, ps, H, D, "cuda", fill=SENTINEL, k_scale=1.0, v_scale=1.0)
+    K.nvfp4_append_paged_kv(k, v, slots, ks, vs, cache.k_cache, cache.v_cache, cache.k_sf,
+                            cache.v_sf, ps, dev_error=err_word)
+    return cache
+
+
+def _compare(cache, ref):
+    for name, got, want in zip(("k_cache", "v_cache", "k_sf", "v_sf"),
+                               (cache.k_cache, cache.v_cache, cache.k_sf, cache.v_sf), ref):
+        g = got.cpu().numpy()
+        if not np.array_equal(g, want):
+            bad = np.argwhere(g != want)
+            raise AssertionError(f"{name}: {len(bad)} bytes differ, first at {bad[:3].tolist()}: "
+                                 f"got {g[tuple(bad[0])]:#x} want {want[tuple(bad[0])]:#x}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "prefill_2k", "append_stress"])
+def test_append_bitexact_full(K, oracle, name):
+    banner(f"append bit-exact {name}")
+    if name == "append_stress":
+        w = W.append_stress("cuda")
+        k, v, slots, P = w.k, w.v, w.slot_mapping, w.num_pages
+    else:
+        w = getattr(W, name)("cuda")
+        k, v, slots, P = w.k, w.v, w.slot_mapping, w.num_pages
+    err = K.device_error_word("cuda")
+    err.zero_()
+    cache = _gpu_append(K, k, v, slots, w.k_scale, w.v_scale, P, w.page_size, err)
+    ref, oerr = _oracle_cache(oracle, k, v, slots, w.k_scale, w.v_scale, P, w.page_size)
+    assert oerr == 0
+    _compare(cache, ref)
+    assert K.read_device_error("cuda") == 0
+
+
+def test_append_bitexact_special_values(K, oracle):
+    """Blocks with inf, NaN, -0, huge and tiny values (the kernel's rare path
+    and saturation), with scales that push the E4M3 scale into saturation and
+    into its subnormal range."""
+    banner("append special values")
+    g = torch.Generator().manual_seed(7)
+    T, H, D = 96, 2, 64
+    x = torch.randn(T, H, D, generator=g) * torch.exp(torch.randn(T, H, 1, generator=g) * 6)
+    x[0, 0, 3] = float("inf")
+    x[1, 1, 17] = float("nan")
+    x[2, 0, :16] = float("nan")
+    x[3, 0, 5] = -float("inf")
+    x[4, :, :] = -0.0
+    x[5, 0, :16] = 3.0e38
+    k = x.to(torch.bfloat16).cuda()
+    v = (-x).to(torch.bfloat16).cuda()
+    P, ps = 8, 16
+    slots = torch.randperm(P * ps, generator=g)[:T].to(torch.int64).cuda()
+    for ks, vs in [(1.0, 1.0), (1e-30, 7.5), (3.0e33, 1e-5), (2.0 ** -149, 1.0e38)]:
+        cache = _gpu_append(K, k, v, slots, ks, vs, P, ps)
+        ref, oerr = _oracle_cache(oracle, k, v, slots, ks, vs, P, ps)
+        assert oerr == 0
+        _compare(cache, ref)
+
+
+@pytest.mark.parametrize("bad", [0.0, -1.0, -0.0, float("nan"), float("inf"), float("-inf")])
+def test_bad_device_scale_sets_flag_and_writes_nothing(K, bad):
+    banner(f"bad device scale {bad}")
+    w = W.tiny("cuda")
+    for which in ("k", "v"):
+        ks = torch.full((), bad if which == "k" else 1.0, device="cuda")
+        vs = torch.full((), bad if which == "v" else 1.0, device="cuda")
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        cache = _gpu_append(K, w.k, w.v, w.slot_mapping, ks, vs, w.num_pages, w.page_size, err)
+        bits = K.read_device_error(word=err)
+        assert bits == (K.DEV_BAD_K_SCALE if which == "k" else K.DEV_BAD_V_SCALE)
+        for t in (cache.k_cache, cache.v_cache, cache.k_sf, cache.v_sf):
+            assert bool((t == SENTINEL).all())
+
+
+def test_host_scale_raises_value_error(K):
+    w = W.tiny("cuda")
+    cache = K.PagedCache.empty(w.num_pages, w.page_size, 2, 64, "cuda")
+    for bad in (0.0, -1.0, float("nan"), float("inf"), torch.tensor(-2.0)):
+        with pytest.raises(ValueError, match="positive finite global decode scale"):
+            K.nvfp4_append_paged_kv(w.k, w.v, w.slot_mapping, bad, 1.0, cache.k_cache, cache.v_cache,
+                                    cache.k_sf, cache.v_sf, w.page_size)
+
+
+def test_zero_rows_launch_nothing_and_check_nothing(K):
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cache = K.PagedCache.empty(4, 16, 2, 64, "cuda", fill=SENTINEL)
+    z = torch.zeros(0, 2, 64, dtype=torch.bfloat16, device="cuda")
+    nan = torch.full((), float("nan"), device="cuda")
+    K.nvfp4_append_paged_kv(z, z, torch.zeros(0, dtype=torch.int64, device="cuda"), nan, nan,
+                            cache.k_cache, cache.v_cache, cache.k_sf, cache.v_sf, 16, dev_error=err)
+    assert K.read_device_error(word=err) == 0
+
+
+def test_padding_and_out_of_range_slots(K, oracle):
+    w = W.tiny("cuda")
+    slots = w.slot_mapping.clone()
+    slots[0] = -1
+    slots[1] = w.num_pages * w.page_size
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cache = _gpu_append(K, w.k, w.v, slots, w.k_scale, w.v_scale, w.num_pages, w.page_size, err)
+    assert K.read_device_error(word=err) == K.DEV_SLOT_OOB
+    ref, oerr = _oracle_cache(oracle, w.k, w.v, slots, w.k_scale, w.v_scale, w.num_pages, w.page_size)
+    assert oerr == 4
+    _compare(cache, ref)
+
+
+def test_append_does_not_synchronize(K):
+    """A long device spin is still running when the call returns."""
+    w = W.tiny("cuda")
+    cache = K.PagedCache.empty(w.num_pages, w.page_size, 2, 64, "cuda")
+    ks = torch.full((), 1.0, device="cuda")
+    torch.cuda.synchronize()
+    torch.cuda._sleep(200_000_000)
+    K.nvfp4_append_paged_kv(w.k, w.v, w.slot_mapping, ks, ks, cache.k_cache, cache.v_cache,
+                            cache.k_sf, cache.v_sf, w.page_size)
+    assert not torch.cuda.current_stream().query()
+    torch.cuda.synchronize()
+
+
+def test_graph_replay_checks_device_scale(K, oracle):
+    """Captured once; replayed with a good scale (correct bytes) and after the
+    scale tensor is overwritten with NaN (flag set, nothing written)."""
+    w = W.tiny("cuda")
+    ks = torch.full((), 1.0, device="cuda")
+    vs = torch.full((), 0.5, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cache = K.PagedCache.empty(w.num_pages, w.page_size, 2, 64, "cuda", fill=SENTINEL)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm up outside capture
+        K.nvfp4_append_paged_kv(w.k, w.v, w.slot_mapping, ks, vs, cache.k_cache, cache.v_cache,
+                                cache.k_sf, cache.v_sf, w.page_size, dev_error=err)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        K.nvfp4_append_paged_kv(w.k, w.v, w.slot_mapping, ks, vs, cache.k_cache, cache.v_cache,
+                                cache.k_sf, cache.v_sf, w.page_size, dev_error=err)
+    ref, _ = _oracle_cache(oracle, w.k, w.v, w.slot_mapping, 1.0, 0.5, w.num_pages, w.page_size)
+    for _ in range(3):
+        for t in (cache.k_cache, cache.v_cache, cache.k_sf, cache.v_sf):
+            t.fill_(SENTINEL)
+        graph.replay()
+        torch.cuda.synchronize()
+        _compare(cache, ref)
+        assert K.read_device_error(word=err) == 0
+    for t in (cache.k_cache, cache.v_cache, cache.k_sf, cache.v_sf):
+        t.fill_(SENTINEL)
+    vs.fill_(float("nan"))
+    graph.replay()
+    torch.cuda.synchronize()
+    assert K.read_device_error(word=err) == K.DEV_BAD_V_SCALE
+    for t in (cache.k_cache, cache.v_cache, cache.k_sf, cache.v_sf):
+        assert bool((t == SENTINEL).all())

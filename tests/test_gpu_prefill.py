@@ -1,0 +1,125 @@
+"""GPU parity of the causal paged prefill against the fp64 oracle, within
+|err| <= 1e-2 + 1e-2 |ref| per element: full outputs on the small and the
+2048x2048 workloads and on ragged batches covering every (head_dim, GQA
+group) kernel; sampled requests on the 1024x1024 batch and the ragged
+chunked-prefill batch at full size; scheduling-order independence (bitwise);
+page-id range errors; no host synchronization."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_helpers import assert_close, banner, oracle_outputs, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    import nvfp4_paged_kv_amd as K
+    K.lib()
+    return K
+
+
+def _check(K, O, w, reqs=None, **kw):
+    out, cache, plan = run_gpu(K, w, **kw)
+    torch.cuda.synchronize()
+    assert K.read_device_error("cuda") == 0
+    ref, rows = oracle_outputs(O, w, reqs)
+    got = out.index_select(0, torch.from_numpy(rows).cuda())
+    return assert_close(got, ref, w.name), out, plan
+
+
+def test_prefill_tiny_full(K, oracle):
+    banner("prefill tiny")
+    e, _, _ = _check(K, oracle, W.tiny("cuda"))
+    print(f"max err {e:.3g}")
+
+
+@pytest.mark.parametrize("hq,hk,d", [(32, 8, 128), (16, 8, 128), (8, 8, 128), (64, 8, 128),
+                                     (8, 4, 64), (4, 2, 64), (2, 2, 64), (16, 2, 64)])
+def test_prefill_ragged_small_all_kernels(K, oracle, hq, hk, d):
+    banner(f"prefill ragged small hq={hq} hk={hk} d={d}")
+    q = [1, 37, 200, 64, 3, 129]
+    kv = [1, 37, 333, 700, 3, 130]
+    w = W.make_attention(f"ragged_small_{hq}_{hk}_{d}", q, kv, hq, hk, d, 16, 120, seed=11,
+                         device="cuda", scales="lognormal", lognormal=(-3.0, 0.5))
+    _check(K, oracle, w)
+
+
+def test_prefill_uniform_small_batch(K, oracle):
+    banner("prefill uniform small batch")
+    w = W.make_attention("uniform_small", [96] * 5, [160] * 5, 32, 8, 128, 16, 64, seed=12,
+                         device="cuda", scales="amax")
+    e, out, plan = _check(K, oracle, w)
+    assert plan.uniform_q == 1
+
+
+def test_prefill_2k_full(K, oracle):
+    banner("prefill 1x2048 full")
+    e, _, _ = _check(K, oracle, W.prefill_2k("cuda"))
+    print(f"max err {e:.3g}")
+
+
+def test_prefill_uniform_1k_sampled(K, oracle):
+    banner("prefill 1024x1024 uniform, 16 sampled requests")
+    w = W.uniform_batch_1k("cuda")
+    reqs = np.random.default_rng(2).choice(w.batch, 16, replace=False)
+    e, out, plan = _check(K, oracle, w, reqs=reqs)
+    assert plan.uniform_q == 1 and plan.head_first == 0
+    print(f"max err {e:.3g}")
+
+
+def test_prefill_ragged_chunked_sampled(K, oracle):
+    banner("prefill ragged chunked 256 requests, 32 sampled")
+    w = W.ragged_chunked("cuda")
+    order = np.argsort(w.kv_lens, kind="stable")
+    rest = np.setdiff1d(np.arange(w.batch), np.concatenate([order[:8], order[-8:]]))
+    reqs = np.concatenate([order[-8:], order[:8], np.random.default_rng(3).choice(rest, 16, replace=False)])
+    e, out, plan = _check(K, oracle, w, reqs=reqs)
+    assert plan.uniform_q == 0
+    print(f"max err {e:.3g}")
+
+
+def test_schedule_orders_give_identical_bits(K):
+    """Uniform O(1) decode (head-first and stream-major) and the device work
+    list compute every tile the same way: outputs are bitwise identical."""
+    banner("schedule order independence")
+    w = W.make_attention("order", [256] * 6, [300] * 6, 32, 8, 128, 16, 200, seed=13, device="cuda",
+                         scales="amax")
+    base, cache, plan = run_gpu(K, w)
+    outs = []
+    for hf, uq in [(1 - plan.head_first, 1), (plan.head_first, 0)]:
+        p2 = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), 32, 8, 128, 16)
+        p2.struct.head_first = hf
+        if not uq:
+            p2.struct.uniform_q = 0
+            p2.struct.workspace_bytes = ((p2.struct.num_tiles * 8 + 4096 + 255) // 256) * 256
+        o, _, _ = run_gpu(K, w, cache=cache, plan=p2)
+        outs.append(o)
+    for o in outs:
+        assert torch.equal(o, base)
+
+
+def test_page_id_out_of_range_sets_flag(K):
+    w = W.tiny("cuda")
+    out, cache, plan = run_gpu(K, w)
+    torch.cuda.synchronize()
+    assert K.read_device_error("cuda") == 0
+    pt = torch.from_numpy(w.page_table).cuda()
+    pt[3] = w.num_pages + 5
+    K.paged_prefill_causal(w.q, torch.from_numpy(w.qo_indptr).cuda(), torch.from_numpy(w.kv_indptr).cuda(),
+                           pt, torch.from_numpy(w.kv_lens).cuda(), cache, out, w.sm_scale, plan=plan)
+    assert K.read_device_error("cuda") == K.DEV_PAGE_OOB
+
+
+def test_prefill_does_not_synchronize(K):
+    w = W.tiny("cuda")
+    out, cache, plan = run_gpu(K, w)
+    args = (torch.from_numpy(w.qo_indptr).cuda(), torch.from_numpy(w.kv_indptr).cuda(),
+            torch.from_numpy(w.page_table).cuda(), torch.from_numpy(w.kv_lens).cuda())
+    torch.cuda.synchronize()
+    torch.cuda._sleep(200_000_000)
+    K.paged_prefill_causal(w.q, *args[:3], args[3], cache, out, w.sm_scale, plan=plan)
+    assert not torch.cuda.current_stream().query()
+    torch.cuda.synchronize()
