@@ -83,7 +83,8 @@ def _ptr(a: np.ndarray):
 
 
 def _threads() -> int:
-    return max(1, min(os.cpu_count() or 1, 64))
+    # at most 16 worker threads (the CPU share of a one-GPU machine)
+    return max(1, min(os.cpu_count() or 1, 16))
 
 
 def e2m1_value(code: int) -> float:
