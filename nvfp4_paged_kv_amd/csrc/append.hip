@@ -141,10 +141,9 @@ __global__ __launch_bounds__(256) void append_kernel(
   // NHD: the cache row of a slot is [slot][H_kv][D/2] bytes, its scale row
   // [slot][H_kv][D/16]; block j of the token is block j of that row.
   const size_t o = (size_t)slot * bpt.d + j;
-  __builtin_nontemporal_store(kp.x, &k_cache[o].x);
-  __builtin_nontemporal_store(kp.y, &k_cache[o].y);
-  __builtin_nontemporal_store(vp.x, &v_cache[o].x);
-  __builtin_nontemporal_store(vp.y, &v_cache[o].y);
+  // one 8-byte store per lane: a wave covers whole cache lines of the row
+  __builtin_nontemporal_store(((uint64_t)kp.y << 32) | kp.x, (uint64_t*)&k_cache[o]);
+  __builtin_nontemporal_store(((uint64_t)vp.y << 32) | vp.x, (uint64_t*)&v_cache[o]);
   k_sf[o] = (uint8_t)ksf;
   v_sf[o] = (uint8_t)vsf;
 }

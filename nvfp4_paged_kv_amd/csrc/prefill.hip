@@ -6,11 +6,12 @@
 //    sections): decoding NVFP4 inside the matrix-multiply loop made the
 //    kernel instruction-bound; each KV tile is instead dequantized ONCE into a
 //    16-bit staging tile that the matrix cores then read natively.  Here: the
-//    whole workgroup decodes the tile (E2M1 x E4M3 is exact in bf16) into LDS;
-//    K is staged [key][d], V transposed [d][key] so both feed
-//    v_mfma_f32_32x32x16_bf16 with 16-byte LDS reads.  The global scales are
-//    not applied in the staging tile: g_k folds into the softmax scale and
-//    g_v into the epilogue.
+//    whole workgroup decodes the tile (E2M1 x E4M3 is exact in bf16) into LDS,
+//    K and V both staged [key][d]; K feeds v_mfma_f32_32x32x16_bf16 with
+//    16-byte LDS reads, V with gfx950 LDS transpose reads.  The raw NVFP4
+//    bytes of the next tile are loaded into registers while the current tile
+//    is computed.  The global scales are not applied in the staging tile: g_k
+//    folds into the softmax scale and g_v into the epilogue.
 //  * FlashInfer PR #3575 page (FP8 causal attention): section 1, O(1) tile
 //    decode when every request has the same query length (uniform flag from
 //    the plan); section 2, the heaviest causal Q tiles of all requests and
@@ -65,14 +66,12 @@ template <int D, int G>
 struct Cfg {
   static constexpr int BQ = kTileRows / G;  // query tokens per tile
   static constexpr int BN = kBlockN;        // keys per KV tile
-  static constexpr int KROW = D * 2;        // bytes of one staged K row
-  static constexpr int KCH = D / 8;         // 16-byte chunks per K row
-  static constexpr int VROW = BN * 2;       // bytes of one staged V^T row
-  static constexpr int K_LDS = BN * KROW;
-  static constexpr int V_LDS = D * VROW;
+  static constexpr int KROW = D * 2;        // bytes of one staged row (K and V alike)
+  static constexpr int STAGE = BN * KROW;   // bytes of one staged tile
   static constexpr int NDC = D / 16;        // MFMA k-steps over head_dim
   static constexpr int NDB = D / 32;        // 32-wide head_dim blocks of O^T
-  static constexpr int JOBS = 4 * D;        // 32-element dequant jobs per KV tile (K and V)
+  static constexpr int PARTS = D / 32;      // 32-element dequant jobs per key row
+  static constexpr int JOBS_PER_THREAD = 2 * BN * PARTS / 256;  // K and V
 };
 
 __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
@@ -80,23 +79,94 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
   return __builtin_amdgcn_perm(f2u(hi), f2u(lo), 0x07060302u);
 }
 
-// Position of key x (0..63) inside a staged V^T row: within each 16-key group
-// bits 2 and 3 are swapped so that lane half h of the P^T operand (keys
-// 4h..4h+3 and 8+4h..8+4h+3 of the group) reads 8 contiguous positions.
-__device__ __forceinline__ int vpos(int x) {
-  return (x & ~15) | (x & 3) | ((x & 4) << 1) | ((x & 8) >> 1);
-}
-// XOR swizzles of the 16-byte chunk index (bank-conflict avoidance).
+// XOR swizzle of the 16-byte chunk index of a staged row (bank spreading for
+// the column-wise MFMA operand reads).
 template <int D>
 __device__ __forceinline__ int kswz(int key) { return key & (D / 8 - 1); }
-__device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// gfx950 LDS transpose read (ds_read_b64_tr_b16): within each group of 16
+// lanes, lane i receives elements i, 16+i, 32+i, 48+i of the 64 16-bit values
+// the group's lanes address (4 consecutive values per lane, in lane order).
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
+// One thread's share of a KV tile: 32 consecutive head_dim elements of one
+// key (16 packed bytes + 2 scale bytes) for K and for V.
+template <int D>
+struct RawJob {
+  u32x4 pk;
+  uint32_t sf;
+};
 
 template <int D, int G>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+__device__ __forceinline__ void load_jobs(const PrefillArgs& a, RawJob<D> (&job)[Cfg<D, G>::JOBS_PER_THREAD],
+                                          int tid, int jt, int kend_max, const int32_t* ptb,
+                                          int hk) {
   using C = Cfg<D, G>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[C::K_LDS + C::V_LDS];
-  uint8_t* const sK = smem;
-  uint8_t* const sV = smem + C::K_LDS;
+#pragma unroll
+  for (int j = 0; j < C::JOBS_PER_THREAD; ++j) {
+    const int id = tid + 256 * j;
+    const int tensor = id / (C::BN * C::PARTS);  // 0: K, 1: V
+    const int rem = id - tensor * C::BN * C::PARTS;
+    const int key = rem / C::PARTS, part = rem % C::PARTS;
+    const int kk = jt * C::BN + key;
+    job[j].pk = (u32x4){0, 0, 0, 0};
+    job[j].sf = 0;
+    if (kk <= kend_max) {  // later keys are masked for every row: zeros
+      const int pi = (int)fastdiv((uint32_t)kk, a.ps_div);
+      const int page = ptb[pi];
+      if ((uint32_t)page < (uint64_t)a.num_pages) {
+        const int64_t row = ((int64_t)page * (int)a.ps_div.d + (kk - pi * (int)a.ps_div.d)) * a.Hk + hk;
+        const uint8_t* cb = tensor ? a.vc : a.kc;
+        const uint8_t* sb = tensor ? a.vsf : a.ksf;
+        job[j].pk = __builtin_nontemporal_load((const u32x4*)(cb + row * (D / 2) + part * 16));
+        job[j].sf = *(const uint16_t*)(sb + row * (D / 16) + part * 2);
+      } else {
+        atomicOr(a.err, (uint32_t)NVFP4KV_DEV_PAGE_OOB);
+      }
+    }
+  }
+}
+
+// Dequantize a job (e2m1 x E4M3 is exact in bf16) into its staged row.
+template <int D, int G>
+__device__ __forceinline__ void stage_jobs(const RawJob<D> (&job)[Cfg<D, G>::JOBS_PER_THREAD],
+                                           uint8_t* smem, int tid) {
+  using C = Cfg<D, G>;
+#pragma unroll
+  for (int j = 0; j < C::JOBS_PER_THREAD; ++j) {
+    const int id = tid + 256 * j;
+    const int tensor = id / (C::BN * C::PARTS);
+    const int rem = id - tensor * C::BN * C::PARTS;
+    const int key = rem / C::PARTS, part = rem % C::PARTS;
+    uint8_t* rowp = smem + tensor * C::STAGE + key * C::KROW;
+    const float S0 = e4m3_decode(job[j].sf & 0xFFu), S1 = e4m3_decode((job[j].sf >> 8) & 0xFFu);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {  // 8 elements per packed dword
+      const float S = w < 2 ? S0 : S1;
+      const uint32_t x = job[j].pk[w];
+      f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 0);
+      f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 1);
+      f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 2);
+      f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 3);
+      const u32x4 o = {bf16_pair(f0[0] * S, f0[1] * S), bf16_pair(f1[0] * S, f1[1] * S),
+                       bf16_pair(f2[0] * S, f2[1] * S), bf16_pair(f3[0] * S, f3[1] * S)};
+      const int ch = (part * 4 + w) ^ kswz<D>(key);
+      *(u32x4*)(rowp + ch * 16) = o;
+    }
+  }
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
+  using C = Cfg<D, G>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
+  const uint8_t* const sK = smem;
+  const uint8_t* const sV = smem + C::STAGE;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, hh = lane >> 5;
 
@@ -139,6 +209,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int kend_max = off + q0 + rows_valid - 1;  // last key any row sees
   const int kend_min = off + q0;                   // last key of the first row
   const int ntiles = kend_max / C::BN + 1;
+  const int32_t* ptb = a.pt + a.kvp[b];
+
+  RawJob<D> job[C::JOBS_PER_THREAD];
+  load_jobs<D, G>(a, job, tid, 0, kend_max, ptb, hk);
 
   const int r = wave * 32 + n;  // this lane's tile row
   const int tr = r % C::BQ, g = r / C::BQ;
@@ -150,7 +224,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const float gk = *a.kscale, gv = *a.vscale;
   if (tile == 0 && tid == 0 && !(scale_ok(gk) && scale_ok(gv)))
     atomicOr(a.err, (uint32_t)NVFP4KV_DEV_BAD_SCALE_ATTN);
-  const float cscale = a.sm_scale_log2 * gk;
+  const float cscale = a.sm_scale_log2 * gk;  // scores -> log2 domain
 
   // ---- Q^T operand fragments: lane holds Q[row][16c + 8hh .. +7]
   bf16x8 qf[C::NDC];
@@ -158,7 +232,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     const uint16_t* qrow = a.q + ((int64_t)(q_begin + (row_valid ? tok : q0)) * a.Hq + hq) * D;
 #pragma unroll
     for (int c = 0; c < C::NDC; ++c) {
-      u32x4 w = row_valid ? *(const u32x4*)(qrow + c * 16 + hh * 8) : (u32x4){0, 0, 0, 0};
+      u32x4 w = *(const u32x4*)(qrow + c * 16 + hh * 8);
       __builtin_memcpy(&qf[c], &w, 16);
     }
   }
@@ -168,69 +242,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   for (int i = 0; i < C::NDB; ++i) o[i] = (f32x16){};
   float m_run = -__builtin_inff(), l_run = 0.0f;
 
-  const int32_t* ptb = a.pt + a.kvp[b];
-  const int ps = (int)a.ps_div.d;
+  // V^T operand addressing (transpose reads): lane t of each 16-lane group
+  // points at 4 consecutive head_dim values of one key.
+  const int t16 = lane & 15, g16 = (lane >> 4) & 1;
 
   for (int jt = 0; jt < ntiles; ++jt) {
     __syncthreads();  // previous tile's LDS reads are done
-    // ---- dequantize the NVFP4 K and V tile into bf16 LDS staging (once)
-#pragma unroll
-    for (int job0 = 0; job0 < C::JOBS; job0 += 256) {
-      const int job = job0 + tid;
-      if (C::JOBS % 256 == 0 || job < C::JOBS) {
-        const int tensor = job / (2 * D);  // 0: K, 1: V
-        const int idx = job - tensor * 2 * D;
-        const int key = idx / (D / 32), part = idx % (D / 32);
-        const int kk = jt * C::BN + key;
-        u32x4 pk = {0, 0, 0, 0};
-        uint32_t sfw = 0;
-        if (kk <= kend_max) {  // later keys are masked for every row: zeros
-          const int pi = (int)fastdiv((uint32_t)kk, a.ps_div);
-          const int page = ptb[pi];
-          if ((uint32_t)page < (uint64_t)a.num_pages) {
-            const int64_t row = ((int64_t)page * ps + (kk - pi * ps)) * a.Hk + hk;
-            const uint8_t* cb = tensor ? a.vc : a.kc;
-            const uint8_t* sb = tensor ? a.vsf : a.ksf;
-            pk = *(const u32x4*)(cb + row * (D / 2) + part * 16);
-            sfw = *(const uint16_t*)(sb + row * (D / 16) + part * 2);
-          } else {
-            atomicOr(a.err, (uint32_t)NVFP4KV_DEV_PAGE_OOB);
-          }
-        }
-        const float S0 = e4m3_decode(sfw & 0xFFu), S1 = e4m3_decode(sfw >> 8);
-        uint32_t ow[16];  // 32 bf16 values, element 2i in the low half of ow[i]
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float S = w < 2 ? S0 : S1;
-          f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[w], 1.0f, 0);
-          f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[w], 1.0f, 1);
-          f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[w], 1.0f, 2);
-          f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk[w], 1.0f, 3);
-          ow[4 * w + 0] = bf16_pair(f0[0] * S, f0[1] * S);
-          ow[4 * w + 1] = bf16_pair(f1[0] * S, f1[1] * S);
-          ow[4 * w + 2] = bf16_pair(f2[0] * S, f2[1] * S);
-          ow[4 * w + 3] = bf16_pair(f3[0] * S, f3[1] * S);
-        }
-        if (tensor == 0) {
-          uint8_t* rowp = sK + key * C::KROW;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int ch = (part * 4 + i) ^ kswz<D>(key);
-            *(u32x4*)(rowp + ch * 16) = (u32x4){ow[4 * i], ow[4 * i + 1], ow[4 * i + 2], ow[4 * i + 3]};
-          }
-        } else {
-          const int p = vpos(key);
-#pragma unroll
-          for (int e = 0; e < 32; ++e) {
-            const int d = part * 32 + e;
-            const int ch = (p >> 3) ^ vswz(d);
-            *(uint16_t*)(sV + d * C::VROW + ch * 16 + (p & 7) * 2) =
-                (uint16_t)(e & 1 ? ow[e >> 1] >> 16 : ow[e >> 1] & 0xFFFFu);
-          }
-        }
-      }
-    }
+    stage_jobs<D, G>(job, smem, tid);  // dequantize once into bf16 LDS
     __syncthreads();
+    if (jt + 1 < ntiles) load_jobs<D, G>(a, job, tid, jt + 1, kend_max, ptb, hk);  // prefetch
 
     // ---- S^T = K Q^T for 64 keys: lane holds S^T[key 32kb + 8(i/4) + 4hh + i%4][row n]
     f32x16 s[2];
@@ -248,20 +268,22 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
 
     // ---- causal mask (diagonal tiles only) + online softmax in log2 domain
-    const bool diag = jt * C::BN + C::BN - 1 > kend_min;
+    if (jt * C::BN + C::BN - 1 > kend_min) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = jt * C::BN + kb * 32 + 8 * (i / 4) + 4 * hh + (i % 4);
+          if (key > kend) s[kb][i] = -__builtin_inff();
+        }
+    }
     float mx = -__builtin_inff();
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = s[kb][i] * cscale;
-        const int key = jt * C::BN + kb * 32 + 8 * (i / 4) + 4 * hh + (i % 4);
-        if (diag && key > kend) x = -__builtin_inff();
-        s[kb][i] = x;
-        mx = __builtin_fmaxf(mx, x);
-      }
+      for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, s[kb][i]);
     mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = __builtin_fmaxf(m_run, mx);
+    const float m_new = __builtin_fmaxf(m_run, mx * cscale);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     float lsum = 0.0f;
@@ -269,13 +291,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(s[kb][i] - m_new);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], cscale, -m_new));
         s[kb][i] = p;
         lsum += p;
       }
     l_run = l_run * alpha + lsum;
+    if (__any(alpha != 1.0f)) {
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
+      for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
+    }
 
     // ---- P^T operands straight from the accumulators (16-key chunks)
     bf16x8 pf[4];
@@ -284,15 +308,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) pf[kc][j] = (__bf16)s[kc >> 1][8 * (kc & 1) + j];
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T; V^T fragments by transpose reads of the [key][d] stage:
+    // keys 4hh..4hh+3 and 8+4hh..8+4hh+3 of each 16-key chunk (the P^T order)
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
-      const int d = db * 32 + n;
+      const int d = db * 32 + 16 * g16 + 4 * (t16 & 3);
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
-        const int ch = (2 * kc + hh) ^ vswz(d);
+        const int k0 = kc * 16 + 4 * hh + (t16 >> 2);
+        const int k1 = k0 + 8;
+        const s16x4 lo = lds_read_tr16(sV + k0 * C::KROW + (((d >> 3) ^ kswz<D>(k0)) << 4) + (d & 7) * 2);
+        const s16x4 hi = lds_read_tr16(sV + k1 * C::KROW + (((d >> 3) ^ kswz<D>(k1)) << 4) + (d & 7) * 2);
         bf16x8 vf;
-        __builtin_memcpy(&vf, sV + d * C::VROW + ch * 16, 16);
+        __builtin_memcpy(&vf, &lo, 8);
+        __builtin_memcpy((char*)&vf + 8, &hi, 8);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], o[db], 0, 0, 0);
       }
     }
