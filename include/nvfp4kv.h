@@ -100,7 +100,7 @@ int nvfp4_append_paged_kv(const void* k, const void* v, const int64_t* slot_mapp
 typedef struct {
   const uint8_t* k_cache; /* [num_pages][page_size][num_kv_heads][head_dim/2] */
   const uint8_t* v_cache;
-  const uint8_t* k_sf;    /* [num_pages][page_size][num_kv_heads][head_dim/16] */
+  const uint8_t* k_sf;    /* [num_pages][page_size][num_kv_heads][head_dim/16], 8-byte aligned */
   const uint8_t* v_sf;
   const float* k_scale;   /* device fp32 scalar */
   const float* v_scale;   /* device fp32 scalar */

@@ -28,6 +28,8 @@
 // of the S^T accumulators without any data movement.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "nvfp4kv_codec.hpp"
 #include "nvfp4kv_internal.hpp"
 
@@ -59,6 +61,7 @@ struct PrefillArgs {
   int Hq, Hk;
   float sm_scale_log2;  // sm_scale * log2(e)
   int B, QT, head_first, nxcd;
+  int snake;  // every tile is resident at once: pair heavy with light tiles
   uint32_t num_tiles;
 };
 
@@ -66,8 +69,13 @@ template <int D, int G>
 struct Cfg {
   static constexpr int BQ = kTileRows / G;  // query tokens per tile
   static constexpr int BN = kBlockN;        // keys per KV tile
-  static constexpr int KROW = D * 2;        // bytes of one staged row (K and V alike)
-  static constexpr int STAGE = BN * KROW;   // bytes of one staged tile
+  // Staged rows are padded so that the column-wise MFMA operand reads of 16
+  // lanes hit distinct LDS banks: +16 bytes for K (16-byte reads of 16
+  // consecutive keys), +32 bytes for V (transpose reads: 4 keys x 32 bytes).
+  static constexpr int KROW = D * 2 + 16;
+  static constexpr int VROW = D * 2 + 32;
+  static constexpr int K_STAGE = BN * KROW;
+  static constexpr int V_STAGE = BN * VROW;
   static constexpr int NDC = D / 16;        // MFMA k-steps over head_dim
   static constexpr int NDB = D / 32;        // 32-wide head_dim blocks of O^T
   static constexpr int PARTS = D / 32;      // 32-element dequant jobs per key row
@@ -78,11 +86,6 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
   // lo, hi are exactly representable in bf16: keep their upper halves.
   return __builtin_amdgcn_perm(f2u(hi), f2u(lo), 0x07060302u);
 }
-
-// XOR swizzle of the 16-byte chunk index of a staged row (bank spreading for
-// the column-wise MFMA operand reads).
-template <int D>
-__device__ __forceinline__ int kswz(int key) { return key & (D / 8 - 1); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -99,52 +102,84 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
 template <int D>
 struct RawJob {
   u32x4 pk;
-  uint32_t sf;
+  // the key's whole scale row (D/16 bytes, naturally aligned); a full-width
+  // load needs no zero-extension copy across the loop back-edge
+  typename std::conditional<D == 128, uint2, uint32_t>::type sfrow;
 };
 
+template <int D>
+__device__ __forceinline__ uint32_t scale_pair(const RawJob<D>& j, int part) {
+  if constexpr (D == 128) return ((part < 2 ? j.sfrow.x : j.sfrow.y) >> (16 * (part & 1))) & 0xFFFFu;
+  else return (j.sfrow >> (16 * (part & 1))) & 0xFFFFu;
+}
+
+// Every job of a thread covers the same key, so one page-table lookup per
+// thread and KV tile serves the K and the V job.
 template <int D, int G>
-__device__ __forceinline__ void load_jobs(const PrefillArgs& a, RawJob<D> (&job)[Cfg<D, G>::JOBS_PER_THREAD],
-                                          int tid, int jt, int kend_max, const int32_t* ptb,
-                                          int hk) {
+__device__ __forceinline__ int job_key(int tid) {
   using C = Cfg<D, G>;
+  static_assert(256 % (C::BN * C::PARTS) == 0, "jobs of a thread must share their key");
+  return (tid % (C::BN * C::PARTS)) / C::PARTS;
+}
+
+// Loads below are unconditional, from always-valid addresses (keys are
+// clamped to the last key any row sees; ids outside the pool read page 0),
+// and what is loaded is only inspected one step later: no branch or select
+// forces a wait on a load that is meant to stay in flight during a tile.
+
+// Raw page id of this thread's key in KV tile jt.
+template <int D, int G>
+__device__ __forceinline__ int lookup_page(const PrefillArgs& a, int tid, int jt, int kend_max,
+                                           const int32_t* ptb) {
+  const int kk = min(jt * Cfg<D, G>::BN + job_key<D, G>(tid), kend_max);
+  return ptb[fastdiv((uint32_t)kk, a.ps_div)];
+}
+
+// Issue the loads of this thread's jobs of KV tile jt; returns whether the
+// key is live (at or before the last key any row sees, in a valid page).
+template <int D, int G>
+__device__ __forceinline__ bool load_jobs(const PrefillArgs& a, RawJob<D> (&job)[Cfg<D, G>::JOBS_PER_THREAD],
+                                          int tid, int jt, int page, int kend_max, int hk) {
+  using C = Cfg<D, G>;
+  const int kk = jt * C::BN + job_key<D, G>(tid);
+  const bool live = kk <= kend_max;  // later keys are masked for every row: zeros
+  const bool in_pool = (uint32_t)page < (uint64_t)a.num_pages;
+  if (live && !in_pool) atomicOr(a.err, (uint32_t)NVFP4KV_DEV_PAGE_OOB);
+  const int ps = (int)a.ps_div.d;
+  const int64_t row =
+      ((int64_t)(in_pool ? page : 0) * ps + (kk - (int)fastdiv((uint32_t)kk, a.ps_div) * ps)) * a.Hk + hk;
 #pragma unroll
   for (int j = 0; j < C::JOBS_PER_THREAD; ++j) {
     const int id = tid + 256 * j;
     const int tensor = id / (C::BN * C::PARTS);  // 0: K, 1: V
-    const int rem = id - tensor * C::BN * C::PARTS;
-    const int key = rem / C::PARTS, part = rem % C::PARTS;
-    const int kk = jt * C::BN + key;
-    job[j].pk = (u32x4){0, 0, 0, 0};
-    job[j].sf = 0;
-    if (kk <= kend_max) {  // later keys are masked for every row: zeros
-      const int pi = (int)fastdiv((uint32_t)kk, a.ps_div);
-      const int page = ptb[pi];
-      if ((uint32_t)page < (uint64_t)a.num_pages) {
-        const int64_t row = ((int64_t)page * (int)a.ps_div.d + (kk - pi * (int)a.ps_div.d)) * a.Hk + hk;
-        const uint8_t* cb = tensor ? a.vc : a.kc;
-        const uint8_t* sb = tensor ? a.vsf : a.ksf;
-        job[j].pk = __builtin_nontemporal_load((const u32x4*)(cb + row * (D / 2) + part * 16));
-        job[j].sf = *(const uint16_t*)(sb + row * (D / 16) + part * 2);
-      } else {
-        atomicOr(a.err, (uint32_t)NVFP4KV_DEV_PAGE_OOB);
-      }
-    }
+    const int part = id % C::PARTS;
+    const uint8_t* cb = tensor ? a.vc : a.kc;
+    const uint8_t* sb = tensor ? a.vsf : a.ksf;
+    job[j].pk = *(const u32x4*)(cb + row * (D / 2) + part * 16);
+    job[j].sfrow = *(const decltype(job[j].sfrow)*)(sb + row * (D / 16));
   }
+  return live && in_pool;
 }
 
-// Dequantize a job (e2m1 x E4M3 is exact in bf16) into its staged row.
+// Dequantize a job (e2m1 x E4M3 is exact in bf16) into its staged row;
+// dead keys stage zeros.  The empty asm pins the first use of the prefetched
+// registers here (after the barrier): otherwise the compiler hoists their
+// unpacking into the previous tile's matrix phase and waits for the loads
+// there.
 template <int D, int G>
-__device__ __forceinline__ void stage_jobs(const RawJob<D> (&job)[Cfg<D, G>::JOBS_PER_THREAD],
-                                           uint8_t* smem, int tid) {
+__device__ __forceinline__ void stage_jobs(RawJob<D>* job, bool live, uint8_t* smem, int tid) {
   using C = Cfg<D, G>;
+#pragma unroll
+  for (int j = 0; j < C::JOBS_PER_THREAD; ++j) asm volatile("" : "+v"(job[j].pk), "+v"(job[j].sfrow));
 #pragma unroll
   for (int j = 0; j < C::JOBS_PER_THREAD; ++j) {
     const int id = tid + 256 * j;
     const int tensor = id / (C::BN * C::PARTS);
     const int rem = id - tensor * C::BN * C::PARTS;
     const int key = rem / C::PARTS, part = rem % C::PARTS;
-    uint8_t* rowp = smem + tensor * C::STAGE + key * C::KROW;
-    const float S0 = e4m3_decode(job[j].sf & 0xFFu), S1 = e4m3_decode((job[j].sf >> 8) & 0xFFu);
+    uint8_t* rowp = tensor ? smem + C::K_STAGE + key * C::VROW : smem + key * C::KROW;
+    const uint32_t sf = live ? scale_pair<D>(job[j], part) : 0u;
+    const float S0 = e4m3_decode(sf & 0xFFu), S1 = e4m3_decode((sf >> 8) & 0xFFu);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {  // 8 elements per packed dword
       const float S = w < 2 ? S0 : S1;
@@ -155,8 +190,7 @@ __device__ __forceinline__ void stage_jobs(const RawJob<D> (&job)[Cfg<D, G>::JOB
       f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 3);
       const u32x4 o = {bf16_pair(f0[0] * S, f0[1] * S), bf16_pair(f1[0] * S, f1[1] * S),
                        bf16_pair(f2[0] * S, f2[1] * S), bf16_pair(f3[0] * S, f3[1] * S)};
-      const int ch = (part * 4 + w) ^ kswz<D>(key);
-      *(u32x4*)(rowp + ch * 16) = o;
+      *(u32x4*)(rowp + (part * 4 + w) * 16) = o;
     }
   }
 }
@@ -164,9 +198,9 @@ __device__ __forceinline__ void stage_jobs(const RawJob<D> (&job)[Cfg<D, G>::JOB
 template <int D, int G>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   using C = Cfg<D, G>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::K_STAGE + C::V_STAGE];
   const uint8_t* const sK = smem;
-  const uint8_t* const sV = smem + C::STAGE;
+  const uint8_t* const sV = smem + C::K_STAGE;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, hh = lane >> 5;
 
@@ -185,6 +219,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       // heaviest Q tiles of every (request, head) first
       qrev = tile / bh_n;
       bh = tile - qrev * bh_n;
+      // When the whole grid is resident at once, workgroup p and p + grid/2
+      // share a CU: the second half walks the remaining tiles lightest first
+      // so that every CU gets one heavy and one light tile.
+      const uint32_t half = (a.QT + 1) / 2;
+      if (a.snake && qrev >= half) qrev = a.QT - 1 - (qrev - half);
     } else {
       // stream-major: XCD x (blockIdx % nxcd) owns a contiguous range of
       // (request, head) streams, each walked heaviest tile first
@@ -211,8 +250,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   const int ntiles = kend_max / C::BN + 1;
   const int32_t* ptb = a.pt + a.kvp[b];
 
+  // Software pipeline: data of tile jt+1 and the page id of tile jt+2 are in
+  // flight while tile jt is computed.
   RawJob<D> job[C::JOBS_PER_THREAD];
-  load_jobs<D, G>(a, job, tid, 0, kend_max, ptb, hk);
+  bool live = load_jobs<D, G>(a, job, tid, 0, lookup_page<D, G>(a, tid, 0, kend_max, ptb), kend_max, hk);
+  int page_next = lookup_page<D, G>(a, tid, 1, kend_max, ptb);
 
   const int r = wave * 32 + n;  // this lane's tile row
   const int tr = r % C::BQ, g = r / C::BQ;
@@ -235,6 +277,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       u32x4 w = *(const u32x4*)(qrow + c * 16 + hh * 8);
       __builtin_memcpy(&qf[c], &w, 16);
     }
+    // Consume the Q fragments here, so their load waits are placed before the
+    // KV loop rather than inside it (where they would also wait for the
+    // prefetch of the next tile).
+#pragma unroll
+    for (int c = 0; c < C::NDC; ++c) asm volatile("" ::"v"(qf[c]));
   }
 
   f32x16 o[C::NDB];
@@ -245,38 +292,42 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   // V^T operand addressing (transpose reads): lane t of each 16-lane group
   // points at 4 consecutive head_dim values of one key.
   const int t16 = lane & 15, g16 = (lane >> 4) & 1;
+  const uint8_t* const vbase = sV + (4 * hh + (t16 >> 2)) * C::VROW + (16 * g16 + 4 * (t16 & 3)) * 2;
 
-  for (int jt = 0; jt < ntiles; ++jt) {
+  // One KV tile: stage it, S^T = K Q^T, (mask), online softmax, O^T += V^T P^T.
+  auto tile_step = [&](const int jt, auto masked) {
+    constexpr bool MASK = decltype(masked)::value;
     __syncthreads();  // previous tile's LDS reads are done
-    stage_jobs<D, G>(job, smem, tid);  // dequantize once into bf16 LDS
+    stage_jobs<D, G>(job, live, smem, tid);  // dequantize once into bf16 LDS
     __syncthreads();
-    if (jt + 1 < ntiles) load_jobs<D, G>(a, job, tid, jt + 1, kend_max, ptb, hk);  // prefetch
+    // prefetch (past the last tile these load in-bounds data that is never used)
+    live = load_jobs<D, G>(a, job, tid, jt + 1, page_next, kend_max, hk);
+    page_next = lookup_page<D, G>(a, tid, jt + 2, kend_max, ptb);
 
     // ---- S^T = K Q^T for 64 keys: lane holds S^T[key 32kb + 8(i/4) + 4hh + i%4][row n]
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = (f32x16){};
-      const int key = kb * 32 + n;
+      const uint8_t* krow = sK + (kb * 32 + n) * C::KROW + hh * 16;
 #pragma unroll
       for (int c = 0; c < C::NDC; ++c) {
-        const int ch = (2 * c + hh) ^ kswz<D>(key);
         bf16x8 kf;
-        __builtin_memcpy(&kf, sK + key * C::KROW + ch * 16, 16);
+        __builtin_memcpy(&kf, krow + c * 32, 16);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kb], 0, 0, 0);
       }
     }
 
-    // ---- causal mask (diagonal tiles only) + online softmax in log2 domain
-    if (jt * C::BN + C::BN - 1 > kend_min) {
+    // ---- causal mask (diagonal tiles only): key > kend  <=>  offset(i) > lim
+    if constexpr (MASK) {
+      const int lim = kend - jt * C::BN - 4 * hh;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = jt * C::BN + kb * 32 + 8 * (i / 4) + 4 * hh + (i % 4);
-          if (key > kend) s[kb][i] = -__builtin_inff();
-        }
+        for (int i = 0; i < 16; ++i)
+          if (kb * 32 + 8 * (i / 4) + (i % 4) > lim) s[kb][i] = -__builtin_inff();
     }
+    // ---- online softmax in the log2 domain (row max on raw scores, scale > 0)
     float mx = -__builtin_inff();
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -312,20 +363,23 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     // keys 4hh..4hh+3 and 8+4hh..8+4hh+3 of each 16-key chunk (the P^T order)
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
-      const int d = db * 32 + 16 * g16 + 4 * (t16 & 3);
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
-        const int k0 = kc * 16 + 4 * hh + (t16 >> 2);
-        const int k1 = k0 + 8;
-        const s16x4 lo = lds_read_tr16(sV + k0 * C::KROW + (((d >> 3) ^ kswz<D>(k0)) << 4) + (d & 7) * 2);
-        const s16x4 hi = lds_read_tr16(sV + k1 * C::KROW + (((d >> 3) ^ kswz<D>(k1)) << 4) + (d & 7) * 2);
+        const uint8_t* vp = vbase + kc * 16 * C::VROW + db * 64;
+        const s16x4 lo = lds_read_tr16(vp);
+        const s16x4 hi = lds_read_tr16(vp + 8 * C::VROW);
         bf16x8 vf;
         __builtin_memcpy(&vf, &lo, 8);
         __builtin_memcpy((char*)&vf + 8, &hi, 8);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], o[db], 0, 0, 0);
       }
     }
-  }
+  };
+  // KV tiles entirely at or below the first row's last key need no mask.
+  const int n_full = min(ntiles, (kend_min + 1) / C::BN);
+  int jt = 0;
+  for (; jt < n_full; ++jt) tile_step(jt, std::false_type{});
+  for (; jt < ntiles; ++jt) tile_step(jt, std::true_type{});
 
   // ---- epilogue: O / l * g_v -> bf16; lane holds O^T[d][row n]
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -436,7 +490,7 @@ extern "C" int paged_prefill_causal(const void* q, const int32_t* qo_indptr,
       !c.k_cache || !c.v_cache || !c.k_sf || !c.v_sf || !c.k_scale || !c.v_scale)
     return NVFP4KV_EINVAL;
   if (!aligned(q, 16) || !aligned(out, 8) || !aligned(c.k_cache, 16) || !aligned(c.v_cache, 16) ||
-      !aligned(c.k_sf, 2) || !aligned(c.v_sf, 2))
+      !aligned(c.k_sf, 8) || !aligned(c.v_sf, 8))
     return NVFP4KV_EINVAL;
   if (p.num_tiles >= (1ll << 31) || p.batch <= 0) return NVFP4KV_EUNSUPPORTED;
   if (p.workspace_bytes > 0 && (!workspace || workspace_bytes < p.workspace_bytes ||
@@ -467,6 +521,7 @@ extern "C" int paged_prefill_causal(const void* q, const int32_t* qo_indptr,
   a.head_first = p.head_first;
   a.nxcd = p.num_xcd > 0 ? p.num_xcd : 1;
   a.num_tiles = (uint32_t)p.num_tiles;
+  a.snake = p.num_tiles <= 2 * (int64_t)device_props().cu_count;
   if (!p.uniform_q) {
     a.worklist = (const int2*)workspace;
     hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(1024), 0, s, qo_indptr, kv_lens, p.batch,
