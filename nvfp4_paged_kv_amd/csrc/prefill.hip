@@ -82,6 +82,10 @@ struct Cfg {
   static constexpr int JOBS_PER_THREAD = 2 * BN * PARTS / 256;  // K and V
 };
 
+// Online-softmax reference max slack (log2 domain): probabilities are formed
+// against a max that may lag the true running max by up to this much.
+constexpr float kRescaleSlack = 8.0f;
+
 __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
   // lo, hi are exactly representable in bf16: keep their upper halves.
   return __builtin_amdgcn_perm(f2u(hi), f2u(lo), 0x07060302u);
@@ -198,9 +202,10 @@ __device__ __forceinline__ void stage_jobs(RawJob<D>* job, bool live, uint8_t* s
 template <int D, int G>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   using C = Cfg<D, G>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[C::K_STAGE + C::V_STAGE];
-  const uint8_t* const sK = smem;
-  const uint8_t* const sV = smem + C::K_STAGE;
+  // Two staging buffers: tile j+1 is dequantized into one while tile j is
+  // read from the other, with a single barrier per KV tile.
+  constexpr int STG = C::K_STAGE + C::V_STAGE;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STG];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, hh = lane >> 5;
 
@@ -292,17 +297,22 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   // V^T operand addressing (transpose reads): lane t of each 16-lane group
   // points at 4 consecutive head_dim values of one key.
   const int t16 = lane & 15, g16 = (lane >> 4) & 1;
-  const uint8_t* const vbase = sV + (4 * hh + (t16 >> 2)) * C::VROW + (16 * g16 + 4 * (t16 & 3)) * 2;
+  const int voff = C::K_STAGE + (4 * hh + (t16 >> 2)) * C::VROW + (16 * g16 + 4 * (t16 & 3)) * 2;
 
-  // One KV tile: stage it, S^T = K Q^T, (mask), online softmax, O^T += V^T P^T.
+  // Pipeline prologue: tile 0 staged, tile 1's NVFP4 bytes and tile 2's page
+  // ids in flight.
+  stage_jobs<D, G>(job, live, smem, tid);
+  live = load_jobs<D, G>(a, job, tid, 1, page_next, kend_max, hk);
+  page_next = lookup_page<D, G>(a, tid, 2, kend_max, ptb);
+  __syncthreads();
+
+  // One KV tile j: S^T = K Q^T from buffer j&1; dequantize tile j+1 into the
+  // other buffer (VALU work that runs beside the matrix cores); prefetch tile
+  // j+2; (mask), online softmax, O^T += V^T P^T; one barrier.
   auto tile_step = [&](const int jt, auto masked) {
     constexpr bool MASK = decltype(masked)::value;
-    __syncthreads();  // previous tile's LDS reads are done
-    stage_jobs<D, G>(job, live, smem, tid);  // dequantize once into bf16 LDS
-    __syncthreads();
-    // prefetch (past the last tile these load in-bounds data that is never used)
-    live = load_jobs<D, G>(a, job, tid, jt + 1, page_next, kend_max, hk);
-    page_next = lookup_page<D, G>(a, tid, jt + 2, kend_max, ptb);
+    const uint8_t* const sK = smem + (jt & 1) * STG;
+    const uint8_t* const vbase = sK + voff;
 
     // ---- S^T = K Q^T for 64 keys: lane holds S^T[key 32kb + 8(i/4) + 4hh + i%4][row n]
     f32x16 s[2];
@@ -317,6 +327,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kb], 0, 0, 0);
       }
     }
+
+    // ---- stage tile j+1 (the other buffer was released by the last barrier;
+    // past the last tile this stages unused data), then prefetch tile j+2
+    stage_jobs<D, G>(job, live, smem + ((jt + 1) & 1) * STG, tid);
+    live = load_jobs<D, G>(a, job, tid, jt + 2, page_next, kend_max, hk);
+    page_next = lookup_page<D, G>(a, tid, jt + 3, kend_max, ptb);
 
     // ---- causal mask (diagonal tiles only): key > kend  <=>  offset(i) > lim
     if constexpr (MASK) {
@@ -334,8 +350,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, s[kb][i]);
     mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = __builtin_fmaxf(m_run, mx * cscale);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    // Lazy rescaling: the reference max moves only when the tile's max
+    // exceeds it by more than kRescaleSlack (log2 units), so p stays below
+    // 2^kRescaleSlack and the O^T rescale is skipped on most tiles.
+    const float m_tile = mx * cscale;
+    const bool grow = m_tile > m_run + kRescaleSlack;
+    const float m_new = grow ? m_tile : m_run;
+    const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
     m_run = m_new;
     float lsum = 0.0f;
 #pragma unroll
@@ -347,7 +368,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         lsum += p;
       }
     l_run = l_run * alpha + lsum;
-    if (__any(alpha != 1.0f)) {
+    if (__any(grow)) {
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
     }
@@ -374,6 +395,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], o[db], 0, 0, 0);
       }
     }
+    __syncthreads();  // tile j+1 staged; buffer j&1 free
   };
   // KV tiles entirely at or below the first row's last key need no mask.
   const int n_full = min(ntiles, (kend_min + 1) / C::BN);
