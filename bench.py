@@ -61,6 +61,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append-stress", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (HBM-counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -76,6 +78,16 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        # a plain copy of known size: FETCH_SIZE / WRITE_SIZE read for it give
+        # the scale between those counters and bytes actually moved
+        src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": src.numel(), "launches": 5}))
+        return
     w = W.prefill_2k(dev)
     cache = K.PagedCache.empty(w.num_pages, w.page_size, w.num_kv_heads, w.head_dim, dev,
                                w.k_scale, w.v_scale)
@@ -195,16 +207,16 @@ def bench_append_stress(K, W, dev, torch, np, iters=12):
             "peak_GBps": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4), "cache": "cold (flushed)"}
 
 
-def cpu_baseline(w, flops_full):
-    """The oracle (plain C, fp64 attention) on a bounded sample of the same
-    step: append of all 2048 K/V rows and the prefill of 2 of the 8 KV heads
-    (8 of 32 query heads); TFLOP/s over the sample's algorithmic flops."""
+def cpu_baseline(w, flops_full, hk_s=8):
+    """The oracle (plain C, fp64 attention) on the step's workload: append of
+    all 2048 K/V rows and the prefill of hk_s of the 8 KV heads (all of them
+    by default: the whole step is a few seconds of CPU work); TFLOP/s over
+    the sample's algorithmic flops."""
     import numpy as np
     import torch
 
     import oracle as O
     import workloads as W
-    hk_s = 2
     G = w.num_q_heads // w.num_kv_heads
     q = W.bf16_bits(w.q[:, : hk_s * G])
     k, v = W.bf16_bits(w.k), W.bf16_bits(w.v)

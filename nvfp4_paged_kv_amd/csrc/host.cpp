@@ -59,12 +59,13 @@ extern "C" int nvfp4_prefill_plan(const int32_t* qo_indptr_host, const int32_t* 
   p.num_kv_heads = num_kv_heads;
   p.head_dim = head_dim;
   p.page_size = page_size;
-  p.block_q = kTileRows / G;
+  const int cu_count = l2_bytes > 0 ? 256 : device_props().cu_count;
   p.block_n = kBlockN;
   // One pass of reductions over the host arrays ([PR #5043]: max lengths from
   // a vectorised reduction, not a per-request Python loop).
   int32_t max_q = 0, max_kv = 0;
-  int64_t tot_q = 0, tot_kv = 0, qtiles = 0;
+  int64_t tot_q = 0, tot_kv = 0, qtiles4 = 0, qtiles8 = 0;
+  const int bq4 = 128 / G, bq8 = 256 / G;
   int32_t max_cost = 0;
   bool bad = false;
   for (int32_t r = 0; r < batch; ++r) {
@@ -77,7 +78,8 @@ extern "C" int nvfp4_prefill_plan(const int32_t* qo_indptr_host, const int32_t* 
     max_kv = lk > max_kv ? lk : max_kv;
     tot_q += lq;
     tot_kv += lk;
-    qtiles += (lq + p.block_q - 1) / p.block_q;
+    qtiles4 += (lq + bq4 - 1) / bq4;
+    qtiles8 += (lq + bq8 - 1) / bq8;
     // heaviest tile of this request: its last one, whose last row sees keys 0..lk-1
     const int32_t cost = lq > 0 ? (lk - 1) / kBlockN + 1 : 0;
     max_cost = cost > max_cost ? cost : max_cost;
@@ -90,9 +92,12 @@ extern "C" int nvfp4_prefill_plan(const int32_t* qo_indptr_host, const int32_t* 
   p.total_kv = tot_kv;
   p.uniform_q = tot_q == (int64_t)batch * max_q;  // [PR #3575] review: O(1) uniform check
   p.uniform_kv = tot_kv == (int64_t)batch * max_kv;
+  // 8-wave tiles when there are enough of them to keep every CU busy
+  const bool wide = head_dim == 128 && qtiles8 * num_kv_heads >= (int64_t)kWideTilesPerCu * cu_count;
+  p.block_q = wide ? bq8 : bq4;
   p.q_tiles_per_head = (max_q + p.block_q - 1) / p.block_q;
   p.max_tile_cost = max_cost;
-  p.num_tiles = qtiles * num_kv_heads;
+  p.num_tiles = (wide ? qtiles8 : qtiles4) * num_kv_heads;
   // [PR #3575] L2 gate: KV bytes = tokens x heads x bytes per token-head (K and
   // V, NVFP4: head_dim/2 code bytes + head_dim/16 scale bytes each); the
   // head-first (global reverse) order only when twice that fits in L2.

@@ -18,8 +18,11 @@ struct DeviceProps {
 };
 const DeviceProps& device_props();
 
-// Rows of one attention tile and keys of one KV tile.
-constexpr int kTileRows = 128;
+// Keys of one KV tile.  An attention tile has W waves of 32 query rows: 4
+// (two workgroups per CU) or, for head_dim 128 batches with at least
+// kWideTilesPerCu tiles per CU, 8 (one workgroup per CU; every dequantized KV
+// tile then feeds twice the matrix work).
 constexpr int kBlockN = 64;
+constexpr int kWideTilesPerCu = 4;
 
 }  // namespace nvfp4kv

@@ -65,9 +65,10 @@ struct PrefillArgs {
   uint32_t num_tiles;
 };
 
-template <int D, int G>
+template <int D, int G, int W>
 struct Cfg {
-  static constexpr int BQ = kTileRows / G;  // query tokens per tile
+  static constexpr int NT = 64 * W;         // threads (W waves of 32 rows each)
+  static constexpr int BQ = 32 * W / G;     // query tokens per tile
   static constexpr int BN = kBlockN;        // keys per KV tile
   // Staged rows are padded so that the column-wise MFMA operand reads of 16
   // lanes hit distinct LDS banks: +16 bytes for K (16-byte reads of 16
@@ -79,7 +80,7 @@ struct Cfg {
   static constexpr int NDC = D / 16;        // MFMA k-steps over head_dim
   static constexpr int NDB = D / 32;        // 32-wide head_dim blocks of O^T
   static constexpr int PARTS = D / 32;      // 32-element dequant jobs per key row
-  static constexpr int JOBS_PER_THREAD = 2 * BN * PARTS / 256;  // K and V
+  static constexpr int JOBS_PER_THREAD = 2 * BN * PARTS / NT;  // K and V
 };
 
 // Online-softmax reference max slack (log2 domain): probabilities are formed
@@ -119,10 +120,10 @@ __device__ __forceinline__ uint32_t scale_pair(const RawJob<D>& j, int part) {
 
 // Every job of a thread covers the same key, so one page-table lookup per
 // thread and KV tile serves the K and the V job.
-template <int D, int G>
+template <int D, int G, int W>
 __device__ __forceinline__ int job_key(int tid) {
-  using C = Cfg<D, G>;
-  static_assert(256 % (C::BN * C::PARTS) == 0, "jobs of a thread must share their key");
+  using C = Cfg<D, G, W>;
+  static_assert(C::NT % (C::BN * C::PARTS) == 0, "jobs of a thread must share their key");
   return (tid % (C::BN * C::PARTS)) / C::PARTS;
 }
 
@@ -132,20 +133,20 @@ __device__ __forceinline__ int job_key(int tid) {
 // forces a wait on a load that is meant to stay in flight during a tile.
 
 // Raw page id of this thread's key in KV tile jt.
-template <int D, int G>
+template <int D, int G, int W>
 __device__ __forceinline__ int lookup_page(const PrefillArgs& a, int tid, int jt, int kend_max,
                                            const int32_t* ptb) {
-  const int kk = min(jt * Cfg<D, G>::BN + job_key<D, G>(tid), kend_max);
+  const int kk = min(jt * Cfg<D, G, W>::BN + job_key<D, G, W>(tid), kend_max);
   return ptb[fastdiv((uint32_t)kk, a.ps_div)];
 }
 
 // Issue the loads of this thread's jobs of KV tile jt; returns whether the
 // key is live (at or before the last key any row sees, in a valid page).
-template <int D, int G>
-__device__ __forceinline__ bool load_jobs(const PrefillArgs& a, RawJob<D> (&job)[Cfg<D, G>::JOBS_PER_THREAD],
+template <int D, int G, int W>
+__device__ __forceinline__ bool load_jobs(const PrefillArgs& a, RawJob<D> (&job)[Cfg<D, G, W>::JOBS_PER_THREAD],
                                           int tid, int jt, int page, int kend_max, int hk) {
-  using C = Cfg<D, G>;
-  const int kk = jt * C::BN + job_key<D, G>(tid);
+  using C = Cfg<D, G, W>;
+  const int kk = jt * C::BN + job_key<D, G, W>(tid);
   const bool live = kk <= kend_max;  // later keys are masked for every row: zeros
   const bool in_pool = (uint32_t)page < (uint64_t)a.num_pages;
   if (live && !in_pool) atomicOr(a.err, (uint32_t)NVFP4KV_DEV_PAGE_OOB);
@@ -154,7 +155,7 @@ __device__ __forceinline__ bool load_jobs(const PrefillArgs& a, RawJob<D> (&job)
       ((int64_t)(in_pool ? page : 0) * ps + (kk - (int)fastdiv((uint32_t)kk, a.ps_div) * ps)) * a.Hk + hk;
 #pragma unroll
   for (int j = 0; j < C::JOBS_PER_THREAD; ++j) {
-    const int id = tid + 256 * j;
+    const int id = tid + C::NT * j;
     const int tensor = id / (C::BN * C::PARTS);  // 0: K, 1: V
     const int part = id % C::PARTS;
     const uint8_t* cb = tensor ? a.vc : a.kc;
@@ -170,14 +171,14 @@ __device__ __forceinline__ bool load_jobs(const PrefillArgs& a, RawJob<D> (&job)
 // registers here (after the barrier): otherwise the compiler hoists their
 // unpacking into the previous tile's matrix phase and waits for the loads
 // there.
-template <int D, int G>
+template <int D, int G, int W>
 __device__ __forceinline__ void stage_jobs(RawJob<D>* job, bool live, uint8_t* smem, int tid) {
-  using C = Cfg<D, G>;
+  using C = Cfg<D, G, W>;
 #pragma unroll
   for (int j = 0; j < C::JOBS_PER_THREAD; ++j) asm volatile("" : "+v"(job[j].pk), "+v"(job[j].sfrow));
 #pragma unroll
   for (int j = 0; j < C::JOBS_PER_THREAD; ++j) {
-    const int id = tid + 256 * j;
+    const int id = tid + C::NT * j;
     const int tensor = id / (C::BN * C::PARTS);
     const int rem = id - tensor * C::BN * C::PARTS;
     const int key = rem / C::PARTS, part = rem % C::PARTS;
@@ -199,9 +200,9 @@ __device__ __forceinline__ void stage_jobs(RawJob<D>* job, bool live, uint8_t* s
   }
 }
 
-template <int D, int G>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
-  using C = Cfg<D, G>;
+template <int D, int G, int W>
+__global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
+  using C = Cfg<D, G, W>;
   // Two staging buffers: tile j+1 is dequantized into one while tile j is
   // read from the other, with a single barrier per KV tile.
   constexpr int STG = C::K_STAGE + C::V_STAGE;
@@ -258,8 +259,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   // Software pipeline: data of tile jt+1 and the page id of tile jt+2 are in
   // flight while tile jt is computed.
   RawJob<D> job[C::JOBS_PER_THREAD];
-  bool live = load_jobs<D, G>(a, job, tid, 0, lookup_page<D, G>(a, tid, 0, kend_max, ptb), kend_max, hk);
-  int page_next = lookup_page<D, G>(a, tid, 1, kend_max, ptb);
+  bool live = load_jobs<D, G, W>(a, job, tid, 0, lookup_page<D, G, W>(a, tid, 0, kend_max, ptb), kend_max, hk);
+  int page_next = lookup_page<D, G, W>(a, tid, 1, kend_max, ptb);
 
   const int r = wave * 32 + n;  // this lane's tile row
   const int tr = r % C::BQ, g = r / C::BQ;
@@ -301,9 +302,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 
   // Pipeline prologue: tile 0 staged, tile 1's NVFP4 bytes and tile 2's page
   // ids in flight.
-  stage_jobs<D, G>(job, live, smem, tid);
-  live = load_jobs<D, G>(a, job, tid, 1, page_next, kend_max, hk);
-  page_next = lookup_page<D, G>(a, tid, 2, kend_max, ptb);
+  stage_jobs<D, G, W>(job, live, smem, tid);
+  live = load_jobs<D, G, W>(a, job, tid, 1, page_next, kend_max, hk);
+  page_next = lookup_page<D, G, W>(a, tid, 2, kend_max, ptb);
   __syncthreads();
 
   // One KV tile j: S^T = K Q^T from buffer j&1; dequantize tile j+1 into the
@@ -330,9 +331,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 
     // ---- stage tile j+1 (the other buffer was released by the last barrier;
     // past the last tile this stages unused data), then prefetch tile j+2
-    stage_jobs<D, G>(job, live, smem + ((jt + 1) & 1) * STG, tid);
-    live = load_jobs<D, G>(a, job, tid, jt + 2, page_next, kend_max, hk);
-    page_next = lookup_page<D, G>(a, tid, jt + 3, kend_max, ptb);
+    stage_jobs<D, G, W>(job, live, smem + ((jt + 1) & 1) * STG, tid);
+    live = load_jobs<D, G, W>(a, job, tid, jt + 2, page_next, kend_max, hk);
+    page_next = lookup_page<D, G, W>(a, tid, jt + 3, kend_max, ptb);
 
     // ---- causal mask (diagonal tiles only): key > kend  <=>  offset(i) > lim
     if constexpr (MASK) {
@@ -485,9 +486,9 @@ __global__ __launch_bounds__(1024) void worklist_kernel(const int32_t* __restric
   }
 }
 
-template <int D, int G>
+template <int D, int G, int W>
 void launch_prefill(const PrefillArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((prefill_kernel<D, G>), dim3(a.num_tiles), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((prefill_kernel<D, G, W>), dim3(a.num_tiles), dim3(64 * W), 0, s, a);
 }
 
 }  // namespace
@@ -543,7 +544,9 @@ extern "C" int paged_prefill_causal(const void* q, const int32_t* qo_indptr,
   a.head_first = p.head_first;
   a.nxcd = p.num_xcd > 0 ? p.num_xcd : 1;
   a.num_tiles = (uint32_t)p.num_tiles;
-  a.snake = p.num_tiles <= 2 * (int64_t)device_props().cu_count;
+  // the heavy/light pairing assumes two co-resident workgroups per CU
+  a.snake = p.block_q * (p.num_q_heads / p.num_kv_heads) == 128 &&
+            p.num_tiles <= 2 * (int64_t)device_props().cu_count;
   if (!p.uniform_q) {
     a.worklist = (const int2*)workspace;
     hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(1024), 0, s, qo_indptr, kv_lens, p.batch,
@@ -551,10 +554,12 @@ extern "C" int paged_prefill_causal(const void* q, const int32_t* qo_indptr,
   }
   const int G = p.num_q_heads / p.num_kv_heads;
   const int D = p.head_dim;
-#define NVFP4KV_CASE(DD, GG) \
-  if (D == DD && G == GG) launch_prefill<DD, GG>(a, s); else
-  NVFP4KV_CASE(128, 1) NVFP4KV_CASE(128, 2) NVFP4KV_CASE(128, 4) NVFP4KV_CASE(128, 8)
-  NVFP4KV_CASE(64, 1) NVFP4KV_CASE(64, 2) NVFP4KV_CASE(64, 4) NVFP4KV_CASE(64, 8)
+  const int W = p.block_q * G / 32;  // waves per tile chosen by the plan
+#define NVFP4KV_CASE(DD, GG, WW) \
+  if (D == DD && G == GG && W == WW) launch_prefill<DD, GG, WW>(a, s); else
+  NVFP4KV_CASE(128, 1, 4) NVFP4KV_CASE(128, 2, 4) NVFP4KV_CASE(128, 4, 4) NVFP4KV_CASE(128, 8, 4)
+  NVFP4KV_CASE(128, 1, 8) NVFP4KV_CASE(128, 2, 8) NVFP4KV_CASE(128, 4, 8) NVFP4KV_CASE(128, 8, 8)
+  NVFP4KV_CASE(64, 1, 4) NVFP4KV_CASE(64, 2, 4) NVFP4KV_CASE(64, 4, 4) NVFP4KV_CASE(64, 8, 4)
   return NVFP4KV_EUNSUPPORTED;
 #undef NVFP4KV_CASE
   return hipGetLastError() == hipSuccess ? NVFP4KV_OK : NVFP4KV_EHIP;

@@ -59,7 +59,10 @@ def test_plan_max_lens(K, dtype, batch, page_size):
     assert p.max_kv_len == int(kv.max())
     assert p.total_q == int(q.sum()) and p.total_kv == int(kv.sum())
     assert p.uniform_q == int(bool((q == q.max()).all()))
-    bq = 128 // 4
+    # head_dim 128: 8-wave tiles (256 rows = 64 tokens x 4 query heads) once
+    # there are at least 4 of them per CU (256 CUs assumed without a device)
+    n8 = 8 * int(((q + 63) // 64).sum())
+    bq = 64 if n8 >= 4 * 256 else 32
     assert p.block_q == bq
     assert p.num_tiles == 8 * int(((q + bq - 1) // bq).sum())
     assert p.max_tile_cost == int(((kv - 1) // 64 + 1)[q > 0].max()) if (q > 0).any() else True
@@ -72,7 +75,9 @@ def test_plan_uniform_flags_and_tiles(K):
     p = _plan(K, [0, 1024, 2048], [1024, 1024])
     assert p.uniform_q == 1 and p.uniform_kv == 1 and p.q_tiles_per_head == 32 and p.num_tiles == 2 * 8 * 32
     p = _plan(K, [0, 2048], [2048])
-    assert p.head_first == 1 and p.num_tiles == 8 * 64
+    assert p.head_first == 1 and p.num_tiles == 8 * 64 and p.block_q == 32
+    p = _plan(K, list(range(0, 1025 * 1024, 1024)), [1024] * 1024)
+    assert p.block_q == 64 and p.num_tiles == 1024 * 8 * 16 and p.head_first == 0
     p = _plan(K, [0, 10, 20], [10, 30])
     assert p.uniform_q == 1 and p.uniform_kv == 0
     p = _plan(K, [0, 10, 25], [10, 30])

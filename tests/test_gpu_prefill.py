@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_helpers import assert_close, banner, oracle_outputs, run_gpu
+from gpu_helpers import assert_close, banner, force_tile_waves, oracle_outputs, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -47,12 +47,24 @@ def test_prefill_ragged_small_all_kernels(K, oracle, hq, hk, d):
     _check(K, oracle, w)
 
 
+@pytest.mark.parametrize("hq,hk", [(32, 8), (16, 8), (8, 8), (64, 8)])
+def test_prefill_ragged_small_wide_tiles(K, oracle, hq, hk):
+    """The 8-wave (256-row) kernels on the small ragged batch."""
+    banner(f"prefill ragged small, 8-wave tiles, hq={hq} hk={hk}")
+    q = [1, 37, 200, 64, 3, 129]
+    kv = [1, 37, 333, 700, 3, 130]
+    w = W.make_attention(f"ragged_small_wide_{hq}_{hk}", q, kv, hq, hk, 128, 16, 120, seed=14,
+                         device="cuda", scales="amax")
+    _check(K, oracle, w, plan=force_tile_waves(K, w, 8))
+
+
 def test_prefill_uniform_small_batch(K, oracle):
     banner("prefill uniform small batch")
     w = W.make_attention("uniform_small", [96] * 5, [160] * 5, 32, 8, 128, 16, 64, seed=12,
                          device="cuda", scales="amax")
     e, out, plan = _check(K, oracle, w)
     assert plan.uniform_q == 1
+    e8, out8, plan8 = _check(K, oracle, w, plan=force_tile_waves(K, w, 8))
 
 
 def test_prefill_2k_full(K, oracle):
