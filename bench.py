@@ -137,6 +137,8 @@ def main():
     abytes = append_bytes(int(w.kv_lens.sum()), w.num_kv_heads, w.head_dim)
     value = flops / (ms_per_step * 1e-3) / 1e12
     pre_tflops = flops / (pre_ms * 1e-3) / 1e12
+    G = w.num_q_heads // w.num_kv_heads
+    kernel_name = f"prefill_kernel<{w.head_dim},{G},{plan.block_q * G // 32}>"
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         t = json.load(open(TRAFFIC_FILE))
@@ -160,7 +162,7 @@ def main():
                    "kv_format": "nvfp4 (e2m1 + e4m3 per 16, fp32 global scale)",
                    "step": "append 2048 K/V rows + causal paged prefill",
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "prefill_kernel<128,4>",
+        "roofline": {"bound": "mfma", "kernel": kernel_name,
                      "achieved": round(pre_tflops, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic, "flops_per_launch": flops,

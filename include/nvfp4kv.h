@@ -61,7 +61,8 @@ enum {
   NVFP4KV_DEV_BAD_V_SCALE = 2u, /* v_scale not positive finite: the append wrote nothing */
   NVFP4KV_DEV_SLOT_OOB = 4u,    /* a slot >= num_pages * page_size: that row was skipped */
   NVFP4KV_DEV_PAGE_OOB = 8u,    /* a page id outside [0, num_pages): read as zeros */
-  NVFP4KV_DEV_BAD_SCALE_ATTN = 16u /* the prefill saw a non positive-finite k/v scale */
+  NVFP4KV_DEV_BAD_SCALE_ATTN = 16u, /* the prefill saw a non positive-finite k/v scale */
+  NVFP4KV_DEV_SPLIT_TIMEOUT = 32u   /* a split Q tile's merge gave up waiting (never expected) */
 };
 
 /*
@@ -127,6 +128,10 @@ typedef struct {
   int64_t kv_bytes;         /* NVFP4 K+V bytes the batch reads */
   int64_t l2_bytes;         /* L2 capacity used by the gate (all XCDs) */
   int64_t workspace_bytes;  /* device workspace paged_prefill_causal needs */
+  int32_t split_len;        /* KV tiles per chunk of a split Q tile (0: no split) */
+  int32_t max_chunks;       /* chunks of the most split Q tile */
+  int64_t num_items;        /* workgroups launched: Q tiles, or their KV chunks */
+  int64_t num_split_tiles;  /* Q tiles (x KV heads) whose KV range is split */
 } nvfp4kv_prefill_plan;
 
 /*
@@ -141,15 +146,24 @@ typedef struct {
  *   kv_indptr_host  int32 [batch+1] or NULL: if given, each request must own
  *                   exactly ceil(kv_len / page_size) page-table entries.
  *   l2_bytes        L2 capacity of the whole device for the gate; 0 = query
- *                   the current HIP device.
+ *                   the current HIP device (and its CU count).
+ *   split_len       KV tiles per chunk when heavy Q tiles are split: 0 =
+ *                   automatic (only for batches whose Q tiles cannot fill
+ *                   every workgroup slot of the GPU), > 0 = split every Q
+ *                   tile longer than this, < 0 = never.
+ *   tile_waves      waves per attention workgroup (32 query rows each): 0 =
+ *                   automatic (8 for head_dim 128 when the batch has at least
+ *                   4 such tiles per CU, else 4), or 4, or 8 (head_dim 128).
  * Returns NVFP4KV_ERANGE if some q_len > kv_len, a length is negative, or a
  * page count does not match; NVFP4KV_EUNSUPPORTED if head_dim is not 64 or
- * 128, or num_q_heads / num_kv_heads is not 1, 2, 4 or 8.
+ * 128, or num_q_heads / num_kv_heads is not 1, 2, 4 or 8; NVFP4KV_EINVAL for
+ * a tile_waves other than 0, 4 or 8 (8 with head_dim 64).
  */
 int nvfp4_prefill_plan(const int32_t* qo_indptr_host, const int32_t* kv_lens_host,
                        const int32_t* kv_indptr_host, int32_t batch, int32_t num_q_heads,
                        int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
-                       int64_t l2_bytes, nvfp4kv_prefill_plan* plan);
+                       int64_t l2_bytes, int32_t split_len, int32_t tile_waves,
+                       nvfp4kv_prefill_plan* plan);
 
 /*
  * paged_prefill_causal -- batched causal prefill attention over the NVFP4
@@ -169,7 +183,16 @@ int nvfp4_prefill_plan(const int32_t* qo_indptr_host, const int32_t* kv_lens_hos
  *   sm_scale   softmax scale applied to q.k.
  *   plan       host pointer, from nvfp4_prefill_plan for these lengths.
  *   workspace  device buffer of at least plan->workspace_bytes (may be NULL
- *              when that is 0), 256-byte aligned.
+ *              when that is 0), 256-byte aligned, ZERO-FILLED before its first
+ *              use: it holds the device work list and, for split Q tiles, the
+ *              chunks' partial results and arrival counters, which every call
+ *              leaves at zero again.  Calls that share a workspace must not
+ *              overlap.
+ * Split Q tiles (plan->split_len > 0, batches too small to fill the GPU): the
+ * KV range of a heavy Q tile is cut into chunks computed by separate
+ * workgroups; the last chunk to finish merges the others' partial
+ * (unnormalized O, running max, sum) in chunk order, so results do not depend
+ * on which chunk finishes last.
  * Semantics: query row i of request r (q_len = Lq, kv_len = Lk) sits at
  * position Lk - Lq + i and attends to keys 0 .. Lk - Lq + i (bottom-right
  * causal alignment); query head h reads KV head h / (num_q_heads /

@@ -28,6 +28,7 @@ LIB_PATH = os.path.join(_PKG, "libnvfp4kv.so")
 
 OK, EINVAL, EUNSUPPORTED, ERANGE, EHIP, EWORKSPACE = 0, -1, -2, -3, -4, -5
 DEV_BAD_K_SCALE, DEV_BAD_V_SCALE, DEV_SLOT_OOB, DEV_PAGE_OOB, DEV_BAD_SCALE_ATTN = 1, 2, 4, 8, 16
+DEV_SPLIT_TIMEOUT = 32
 
 ENTRY_POINTS = ("nvfp4_append_paged_kv", "nvfp4_prefill_plan", "paged_prefill_causal",
                 "nvfp4kv_read_device_error", "nvfp4kv_status_string", "nvfp4kv_abi_version")
@@ -56,7 +57,9 @@ class PlanStruct(ctypes.Structure):
                 ("uniform_q", "uniform_kv", "head_first", "block_q", "block_n",
                  "q_tiles_per_head", "max_tile_cost", "num_xcd")] + \
                [(n, ctypes.c_int64) for n in
-                ("num_tiles", "kv_bytes", "l2_bytes", "workspace_bytes")]
+                ("num_tiles", "kv_bytes", "l2_bytes", "workspace_bytes")] + \
+               [("split_len", ctypes.c_int32), ("max_chunks", ctypes.c_int32),
+                ("num_items", ctypes.c_int64), ("num_split_tiles", ctypes.c_int64)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -77,7 +80,7 @@ def lib():
         P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         L.nvfp4_append_paged_kv.argtypes = [P, P, P, I64, P, P, P, P, P, P, I64, I32, I32, I32, P, P]
         L.nvfp4_append_paged_kv.restype = ctypes.c_int
-        L.nvfp4_prefill_plan.argtypes = [P, P, P, I32, I32, I32, I32, I32, I64,
+        L.nvfp4_prefill_plan.argtypes = [P, P, P, I32, I32, I32, I32, I32, I64, I32, I32,
                                          ctypes.POINTER(PlanStruct)]
         L.nvfp4_prefill_plan.restype = ctypes.c_int
         L.paged_prefill_causal.argtypes = [P, P, P, P, P, ctypes.POINTER(Cache), P, ctypes.c_float,
@@ -248,7 +251,7 @@ class Plan:
     max lengths from tensor reductions, lengths cast to int32 at entry)."""
 
     def __init__(self, qo_indptr, kv_lens, num_q_heads, num_kv_heads, head_dim, page_size,
-                 kv_indptr=None, l2_bytes: int = 0):
+                 kv_indptr=None, l2_bytes: int = 0, split_len: int = 0, tile_waves: int = 0):
         qo = _host_int32(qo_indptr, "qo_indptr")
         kvl = _host_int32(kv_lens, "kv_lens")
         kvp = _host_int32(kv_indptr, "kv_indptr") if kv_indptr is not None else None
@@ -257,7 +260,8 @@ class Plan:
         self.struct = PlanStruct()
         _check(lib().nvfp4_prefill_plan(
             _ptr(qo), _ptr(kvl), _ptr(kvp), kvl.numel(), num_q_heads, num_kv_heads, head_dim,
-            page_size, l2_bytes, ctypes.byref(self.struct)), "nvfp4_prefill_plan")
+            page_size, l2_bytes, split_len, tile_waves, ctypes.byref(self.struct)),
+            "nvfp4_prefill_plan")
         self.qo_host, self.kv_lens_host = qo, kvl
         self._workspace = {}
 
@@ -272,7 +276,8 @@ class Plan:
             return None
         device = torch.device(device)
         if device not in self._workspace:
-            self._workspace[device] = torch.empty(n, dtype=torch.uint8, device=device)
+            # zero-filled once (a fill kernel); the kernels leave it zeroed
+            self._workspace[device] = torch.zeros(n, dtype=torch.uint8, device=device)
         return self._workspace[device]
 
 
@@ -288,9 +293,12 @@ def _host_int32(t, name) -> torch.Tensor:
 
 
 def plan(qo_indptr, kv_lens, num_q_heads, num_kv_heads, head_dim, page_size, kv_indptr=None,
-         l2_bytes: int = 0) -> Plan:
+         l2_bytes: int = 0, split_len: int = 0, tile_waves: int = 0) -> Plan:
+    """Host plan of one prefill batch.  split_len: KV tiles per chunk of a split
+    Q tile (0 automatic, > 0 forced, < 0 never); tile_waves: waves of 32 query
+    rows per workgroup (0 automatic, 4 or 8)."""
     return Plan(qo_indptr, kv_lens, num_q_heads, num_kv_heads, head_dim, page_size, kv_indptr,
-                l2_bytes)
+                l2_bytes, split_len, tile_waves)
 
 
 def paged_prefill_causal(q: torch.Tensor, qo_indptr: torch.Tensor, kv_indptr: torch.Tensor,

@@ -2,6 +2,7 @@
 // synchronizing device-error read and the device property cache.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -42,10 +43,12 @@ using namespace nvfp4kv;
 extern "C" int nvfp4_prefill_plan(const int32_t* qo_indptr_host, const int32_t* kv_lens_host,
                                   const int32_t* kv_indptr_host, int32_t batch,
                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                  int32_t page_size, int64_t l2_bytes,
-                                  nvfp4kv_prefill_plan* plan) {
+                                  int32_t page_size, int64_t l2_bytes, int32_t split_len,
+                                  int32_t tile_waves, nvfp4kv_prefill_plan* plan) {
   if (!plan || batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || page_size <= 0 ||
       head_dim <= 0 || (batch > 0 && (!qo_indptr_host || !kv_lens_host)))
+    return NVFP4KV_EINVAL;
+  if (!(tile_waves == 0 || tile_waves == 4 || (tile_waves == 8 && head_dim == 128)))
     return NVFP4KV_EINVAL;
   if (num_q_heads % num_kv_heads != 0) return NVFP4KV_EUNSUPPORTED;
   const int G = num_q_heads / num_kv_heads;
@@ -92,12 +95,54 @@ extern "C" int nvfp4_prefill_plan(const int32_t* qo_indptr_host, const int32_t* 
   p.total_kv = tot_kv;
   p.uniform_q = tot_q == (int64_t)batch * max_q;  // [PR #3575] review: O(1) uniform check
   p.uniform_kv = tot_kv == (int64_t)batch * max_kv;
-  // 8-wave tiles when there are enough of them to keep every CU busy
-  const bool wide = head_dim == 128 && qtiles8 * num_kv_heads >= (int64_t)kWideTilesPerCu * cu_count;
+  // 8-wave tiles (256 rows, one workgroup per CU) halve the dequantization
+  // per row but need many tiles to balance; 4-wave tiles (two per CU) for
+  // head_dim 64 and for batches with fewer than kWideTilesPerCu 8-wave tiles
+  // per CU.
+  const bool wide = tile_waves == 8 ||
+                    (tile_waves == 0 && head_dim == 128 &&
+                     qtiles8 * num_kv_heads >= (int64_t)kWideTilesPerCu * cu_count);
   p.block_q = wide ? bq8 : bq4;
   p.q_tiles_per_head = (max_q + p.block_q - 1) / p.block_q;
   p.max_tile_cost = max_cost;
   p.num_tiles = (wide ? qtiles8 : qtiles4) * num_kv_heads;
+  if (max_cost >= 65536) return NVFP4KV_EUNSUPPORTED;  // KV tile index packs into 16 bits
+  // Batches whose Q tiles cannot fill every workgroup slot (one 8-wave or two
+  // 4-wave workgroups per CU) split the KV range of their heaviest Q tiles so
+  // that every slot gets about the same number of KV tiles: chunk length =
+  // total KV tiles / slots.
+  const int64_t slots = (int64_t)cu_count * (wide ? 1 : 2);
+  p.num_items = p.num_tiles;
+  if (split_len >= 0 && (split_len > 0 || p.num_tiles < slots)) {
+    int64_t total_cost = 0;
+    for (int32_t r = 0; r < batch; ++r) {
+      const int32_t lq = qo_indptr_host[r + 1] - qo_indptr_host[r];
+      const int32_t off = kv_lens_host[r] - lq;
+      for (int32_t t = 0; t * p.block_q < lq; ++t)
+        total_cost += (off + std::min((t + 1) * p.block_q, lq) - 1) / kBlockN + 1;
+    }
+    total_cost *= num_kv_heads;
+    int32_t len = split_len > 0 ? split_len
+                                : std::max((int32_t)((total_cost + slots - 1) / slots), kMinSplit);
+    len = std::max(len, (max_cost + kMaxChunks - 1) / kMaxChunks);
+    if (max_cost > len) {
+      p.split_len = len;
+      p.max_chunks = (max_cost + len - 1) / len;
+      int64_t items = 0, split = 0;
+      for (int32_t r = 0; r < batch; ++r) {
+        const int32_t lq = qo_indptr_host[r + 1] - qo_indptr_host[r];
+        const int32_t off = kv_lens_host[r] - lq;
+        for (int32_t t = 0; t * p.block_q < lq; ++t) {
+          const int32_t c = (off + std::min((t + 1) * p.block_q, lq) - 1) / kBlockN + 1;
+          const int32_t nch = (c + len - 1) / len;
+          items += nch;
+          split += nch > 1;
+        }
+      }
+      p.num_items = items * num_kv_heads;
+      p.num_split_tiles = split * num_kv_heads;
+    }
+  }
   // [PR #3575] L2 gate: KV bytes = tokens x heads x bytes per token-head (K and
   // V, NVFP4: head_dim/2 code bytes + head_dim/16 scale bytes each); the
   // head-first (global reverse) order only when twice that fits in L2.
@@ -111,8 +156,9 @@ extern "C" int nvfp4_prefill_plan(const int32_t* qo_indptr_host, const int32_t* 
     p.num_xcd = d.num_xcd;
   }
   p.head_first = 2 * p.kv_bytes <= p.l2_bytes;
-  // Ragged batches need a device work list: 2 int32 per tile, plus counters.
-  p.workspace_bytes = p.uniform_q ? 0 : (int64_t)(p.num_tiles * 8 + 4096 + 255) / 256 * 256;
+  // Ragged or split batches need a device work list (and, when split, the
+  // chunks' partials and arrival counters).
+  p.workspace_bytes = workspace_layout(p).total;
   *plan = p;
   return NVFP4KV_OK;
 }

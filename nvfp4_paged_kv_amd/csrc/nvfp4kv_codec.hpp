@@ -99,9 +99,11 @@ static inline FastDiv make_fastdiv(uint32_t d) {
   return f;
 }
 NVFP4KV_HD uint32_t fastdiv(uint32_t n, FastDiv f) {
-  if (f.shift == 0) return n;
+  // branch-free (a select for d = 1, where shift is 0), so that it does not
+  // split the straight-line code it is used in
   uint32_t t = (uint32_t)(((uint64_t)n * f.mul) >> 32);
-  return (t + ((n - t) >> 1)) >> (f.shift - 1);
+  uint32_t q = (t + ((n - t) >> 1)) >> ((f.shift - 1) & 31u);
+  return f.shift ? q : n;
 }
 
 }  // namespace nvfp4kv

@@ -24,5 +24,28 @@ const DeviceProps& device_props();
 // tile then feeds twice the matrix work).
 constexpr int kBlockN = 64;
 constexpr int kWideTilesPerCu = 4;
+// Split Q tiles: chunks of at least kMinSplit KV tiles, at most kMaxChunks.
+constexpr int kMinSplit = 8;
+constexpr int kMaxChunks = 16;
+
+// Workspace layout of one prefill call (shared by the plan and the launcher):
+// [work list: 16 B per item][arrival counters: 2 x int32 per split tile]
+// [partials: per split tile, max_chunks x (rows x head_dim fp32 + 2 x rows fp32)].
+inline int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+struct WorkspaceLayout {
+  int64_t list, counters, partials, total, partial_bytes;
+};
+inline WorkspaceLayout workspace_layout(const nvfp4kv_prefill_plan& p) {
+  WorkspaceLayout w{};
+  const bool need_list = !p.uniform_q || p.split_len > 0;
+  const int64_t rows = (int64_t)p.block_q * (p.num_q_heads / p.num_kv_heads);
+  w.partial_bytes = rows * p.head_dim * 4 + rows * 8;
+  w.list = 0;
+  w.counters = align256(need_list ? p.num_items * 16 : 0);
+  w.partials = align256(w.counters + p.num_split_tiles * 8);
+  w.total = p.num_split_tiles > 0 ? w.partials + p.num_split_tiles * p.max_chunks * w.partial_bytes
+                                  : (need_list ? w.counters : 0);
+  return w;
+}
 
 }  // namespace nvfp4kv

@@ -40,6 +40,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct PrefillArgs {
   const uint16_t* q;
@@ -54,7 +55,11 @@ struct PrefillArgs {
   const float* kscale;
   const float* vscale;
   uint16_t* out;
-  const int2* worklist;  // ragged batches; null when uniform
+  const int4* worklist;  // ragged or split batches; null for the uniform O(1) decode
+  int* counters;         // split tiles: [arrivals, partials written] per split tile
+  float* partials;       // split tiles: max_chunks partial results each
+  int64_t partial_floats;  // floats of one partial (rows x D for O, then m and l)
+  int max_chunks;
   uint32_t* err;
   int64_t num_pages;
   FastDiv ps_div;
@@ -62,7 +67,7 @@ struct PrefillArgs {
   float sm_scale_log2;  // sm_scale * log2(e)
   int B, QT, head_first, nxcd;
   int snake;  // every tile is resident at once: pair heavy with light tiles
-  uint32_t num_tiles;
+  uint32_t num_tiles, num_items;
 };
 
 template <int D, int G, int W>
@@ -81,6 +86,9 @@ struct Cfg {
   static constexpr int NDB = D / 32;        // 32-wide head_dim blocks of O^T
   static constexpr int PARTS = D / 32;      // 32-element dequant jobs per key row
   static constexpr int JOBS_PER_THREAD = 2 * BN * PARTS / NT;  // K and V
+  // VALU instructions of a tile's staging and prefetch (about 70 per job plus
+  // addressing), spread over the 2 * NDC MFMAs of S^T = K Q^T
+  static constexpr int STAGE_VALU_PER_MFMA = (JOBS_PER_THREAD * 70 + 24 + 2 * NDC - 1) / (2 * NDC);
 };
 
 // Online-softmax reference max slack (log2 domain): probabilities are formed
@@ -91,6 +99,36 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
   // lo, hi are exactly representable in bf16: keep their upper halves.
   return __builtin_amdgcn_perm(f2u(hi), f2u(lo), 0x07060302u);
 }
+
+// Device-coherent access to the split-tile partials: raw buffer loads and
+// stores with the device-scope cache policy (sc1), the policy of relaxed
+// device-scope atomic loads and stores.  Each XCD's L2 is its own cache, so a
+// partial written on one XCD is read on another through this policy.
+// Offsets are bytes from the resource base; the resource range bounds them.
+constexpr int kDeviceScopePolicy = 16;  // sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(float* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void coherent_store4(__amdgpu_buffer_rsrc_t r, int off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kDeviceScopePolicy);
+}
+__device__ __forceinline__ void coherent_store1(__amdgpu_buffer_rsrc_t r, int off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, kDeviceScopePolicy);
+}
+__device__ __forceinline__ f32x4 coherent_load4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDeviceScopePolicy));
+}
+__device__ __forceinline__ float coherent_load1(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kDeviceScopePolicy));
+}
+
+// Instruction classes of the scheduling-group hints.
+constexpr int kSchedValu = 0x2 | 0x400;  // VALU and transcendental
+constexpr int kSchedMfma = 0x8;
+constexpr int kSchedDsRead = 0x100;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -112,10 +150,12 @@ struct RawJob {
   typename std::conditional<D == 128, uint2, uint32_t>::type sfrow;
 };
 
+// The dword of a key's scale row holding the two scale bytes of job part
+// `part` (in its low half for even parts, its high half for odd ones).
 template <int D>
-__device__ __forceinline__ uint32_t scale_pair(const RawJob<D>& j, int part) {
-  if constexpr (D == 128) return ((part < 2 ? j.sfrow.x : j.sfrow.y) >> (16 * (part & 1))) & 0xFFFFu;
-  else return (j.sfrow >> (16 * (part & 1))) & 0xFFFFu;
+__device__ __forceinline__ uint32_t scale_word(const RawJob<D>& j, int part) {
+  if constexpr (D == 128) return part < 2 ? j.sfrow.x : j.sfrow.y;
+  else return j.sfrow;
 }
 
 // Every job of a thread covers the same key, so one page-table lookup per
@@ -141,15 +181,17 @@ __device__ __forceinline__ int lookup_page(const PrefillArgs& a, int tid, int jt
 }
 
 // Issue the loads of this thread's jobs of KV tile jt; returns whether the
-// key is live (at or before the last key any row sees, in a valid page).
+// key is live (at or before the last key any row sees, in a valid page) and
+// notes in page_bad a live key whose page id is outside the pool.
 template <int D, int G, int W>
 __device__ __forceinline__ bool load_jobs(const PrefillArgs& a, RawJob<D> (&job)[Cfg<D, G, W>::JOBS_PER_THREAD],
-                                          int tid, int jt, int page, int kend_max, int hk) {
+                                          int tid, int jt, int page, int kend_max, int hk,
+                                          bool& page_bad) {
   using C = Cfg<D, G, W>;
   const int kk = jt * C::BN + job_key<D, G, W>(tid);
   const bool live = kk <= kend_max;  // later keys are masked for every row: zeros
   const bool in_pool = (uint32_t)page < (uint64_t)a.num_pages;
-  if (live && !in_pool) atomicOr(a.err, (uint32_t)NVFP4KV_DEV_PAGE_OOB);
+  page_bad |= live && !in_pool;  // reported once, after the KV loop
   const int ps = (int)a.ps_div.d;
   const int64_t row =
       ((int64_t)(in_pool ? page : 0) * ps + (kk - (int)fastdiv((uint32_t)kk, a.ps_div) * ps)) * a.Hk + hk;
@@ -166,16 +208,22 @@ __device__ __forceinline__ bool load_jobs(const PrefillArgs& a, RawJob<D> (&job)
   return live && in_pool;
 }
 
+// Pin the first use of the prefetched registers at the point of the call
+// (right after a barrier): otherwise the compiler hoists their unpacking into
+// the previous tile's matrix phase and waits for the loads there.  The pin is
+// an ordering point for memory operations, so it goes before the tile's LDS
+// reads, not between them and the dequantization.
+template <int D, int G, int W>
+__device__ __forceinline__ void pin_jobs(RawJob<D>* job) {
+#pragma unroll
+  for (int j = 0; j < Cfg<D, G, W>::JOBS_PER_THREAD; ++j) asm volatile("" : "+v"(job[j].pk), "+v"(job[j].sfrow));
+}
+
 // Dequantize a job (e2m1 x E4M3 is exact in bf16) into its staged row;
-// dead keys stage zeros.  The empty asm pins the first use of the prefetched
-// registers here (after the barrier): otherwise the compiler hoists their
-// unpacking into the previous tile's matrix phase and waits for the loads
-// there.
+// dead keys stage zeros.
 template <int D, int G, int W>
 __device__ __forceinline__ void stage_jobs(RawJob<D>* job, bool live, uint8_t* smem, int tid) {
   using C = Cfg<D, G, W>;
-#pragma unroll
-  for (int j = 0; j < C::JOBS_PER_THREAD; ++j) asm volatile("" : "+v"(job[j].pk), "+v"(job[j].sfrow));
 #pragma unroll
   for (int j = 0; j < C::JOBS_PER_THREAD; ++j) {
     const int id = tid + C::NT * j;
@@ -183,11 +231,12 @@ __device__ __forceinline__ void stage_jobs(RawJob<D>* job, bool live, uint8_t* s
     const int rem = id - tensor * C::BN * C::PARTS;
     const int key = rem / C::PARTS, part = rem % C::PARTS;
     uint8_t* rowp = tensor ? smem + C::K_STAGE + key * C::VROW : smem + key * C::KROW;
-    const uint32_t sf = live ? scale_pair<D>(job[j], part) : 0u;
-    const float S0 = e4m3_decode(sf & 0xFFu), S1 = e4m3_decode((sf >> 8) & 0xFFu);
+    // both E4M3 scales of the part in one conversion (dead keys: zero scales)
+    const uint32_t sw = live ? scale_word<D>(job[j], part) >> (16 * (part & 1)) : 0u;
+    const f32x2 S01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw, 1.0f, false);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {  // 8 elements per packed dword
-      const float S = w < 2 ? S0 : S1;
+      const float S = w < 2 ? S01[0] : S01[1];
       const uint32_t x = job[j].pk[w];
       f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 0);
       f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 1);
@@ -200,6 +249,52 @@ __device__ __forceinline__ void stage_jobs(RawJob<D>* job, bool live, uint8_t* s
   }
 }
 
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// The staging of one KV tile cut into half-words: piece p of a thread
+// dequantizes 8 elements (word (p/2)%4 of job p/8, its low or high half) and
+// every second piece stores the finished 16-byte chunk.  The pieces are
+// interleaved with the matrix instructions of the tile before.
+template <int D, int G, int W>
+struct TileStager {
+  using C = Cfg<D, G, W>;
+  static constexpr int PIECES = 8 * C::JOBS_PER_THREAD;
+  uint8_t* rowp[C::JOBS_PER_THREAD];
+  f32x2 S01[C::JOBS_PER_THREAD];
+  u32x4 chunk;
+  __device__ __forceinline__ TileStager(const RawJob<D>* job, bool live, uint8_t* smem, int tid) {
+#pragma unroll
+    for (int j = 0; j < C::JOBS_PER_THREAD; ++j) {
+      const int id = tid + C::NT * j;
+      const int tensor = id / (C::BN * C::PARTS);
+      const int rem = id - tensor * C::BN * C::PARTS;
+      const int key = rem / C::PARTS, part = rem % C::PARTS;
+      rowp[j] = (tensor ? smem + C::K_STAGE + key * C::VROW : smem + key * C::KROW) + part * 64;
+      // both E4M3 scales of the part in one conversion (dead keys: zero scales)
+      const uint32_t sw = live ? scale_word<D>(job[j], part) >> (16 * (part & 1)) : 0u;
+      S01[j] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw, 1.0f, false);
+    }
+  }
+  template <int P>
+  __device__ __forceinline__ void piece(const RawJob<D>* job) {
+    constexpr int j = P / 8, w = (P / 2) % 4, h = P % 2;
+    const float S = w < 2 ? S01[j][0] : S01[j][1];
+    const uint32_t x = job[j].pk[w];
+    const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 2 * h);
+    const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 2 * h + 1);
+    chunk[2 * h] = bf16_pair(f0[0] * S, f0[1] * S);
+    chunk[2 * h + 1] = bf16_pair(f1[0] * S, f1[1] * S);
+    if constexpr (h == 1) *(u32x4*)(rowp[j] + w * 16) = chunk;
+  }
+};
+
 template <int D, int G, int W>
 __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   using C = Cfg<D, G, W>;
@@ -210,14 +305,18 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, hh = lane >> 5;
 
-  // ---- which (request, KV head, Q tile) this workgroup computes
+  // ---- which (request, KV head, Q tile, KV range) this workgroup computes
   int b, hk, qt;
+  int jt_begin = 0, jt_end = 0x7FFFFFFF, split = -1;
   const uint32_t tile = blockIdx.x;
   if (a.worklist) {
-    const int2 e = a.worklist[tile];
+    const int4 e = a.worklist[tile];
     b = e.x;
     qt = e.y / a.Hk;
     hk = e.y - qt * a.Hk;
+    jt_begin = (uint32_t)e.z >> 16;
+    jt_end = e.z & 0xFFFF;
+    split = e.w;  // -1, or (split id << 10) | (chunk << 5) | chunks
   } else {
     const uint32_t bh_n = (uint32_t)a.B * a.Hk;
     uint32_t bh, qrev;
@@ -253,14 +352,16 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   if (rows_valid <= 0) return;  // (uniform batches with short requests)
   const int kend_max = off + q0 + rows_valid - 1;  // last key any row sees
   const int kend_min = off + q0;                   // last key of the first row
-  const int ntiles = kend_max / C::BN + 1;
+  const int ntiles = min(kend_max / C::BN + 1, jt_end);  // this workgroup's KV tiles: [jt_begin, ntiles)
   const int32_t* ptb = a.pt + a.kvp[b];
 
   // Software pipeline: data of tile jt+1 and the page id of tile jt+2 are in
   // flight while tile jt is computed.
   RawJob<D> job[C::JOBS_PER_THREAD];
-  bool live = load_jobs<D, G, W>(a, job, tid, 0, lookup_page<D, G, W>(a, tid, 0, kend_max, ptb), kend_max, hk);
-  int page_next = lookup_page<D, G, W>(a, tid, 1, kend_max, ptb);
+  bool page_bad = false;
+  bool live = load_jobs<D, G, W>(a, job, tid, jt_begin, lookup_page<D, G, W>(a, tid, jt_begin, kend_max, ptb),
+                                 kend_max, hk, page_bad);
+  int page_next = lookup_page<D, G, W>(a, tid, jt_begin + 1, kend_max, ptb);
 
   const int r = wave * 32 + n;  // this lane's tile row
   const int tr = r % C::BQ, g = r / C::BQ;
@@ -300,11 +401,12 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   const int t16 = lane & 15, g16 = (lane >> 4) & 1;
   const int voff = C::K_STAGE + (4 * hh + (t16 >> 2)) * C::VROW + (16 * g16 + 4 * (t16 & 3)) * 2;
 
-  // Pipeline prologue: tile 0 staged, tile 1's NVFP4 bytes and tile 2's page
-  // ids in flight.
-  stage_jobs<D, G, W>(job, live, smem, tid);
-  live = load_jobs<D, G, W>(a, job, tid, 1, page_next, kend_max, hk);
-  page_next = lookup_page<D, G, W>(a, tid, 2, kend_max, ptb);
+  // Pipeline prologue: the first tile staged (into buffer jt_begin & 1), the
+  // next tile's NVFP4 bytes and the one after's page ids in flight.
+  pin_jobs<D, G, W>(job);
+  stage_jobs<D, G, W>(job, live, smem + (jt_begin & 1) * STG, tid);
+  live = load_jobs<D, G, W>(a, job, tid, jt_begin + 1, page_next, kend_max, hk, page_bad);
+  page_next = lookup_page<D, G, W>(a, tid, jt_begin + 2, kend_max, ptb);
   __syncthreads();
 
   // One KV tile j: S^T = K Q^T from buffer j&1; dequantize tile j+1 into the
@@ -314,26 +416,41 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     constexpr bool MASK = decltype(masked)::value;
     const uint8_t* const sK = smem + (jt & 1) * STG;
     const uint8_t* const vbase = sK + voff;
+    pin_jobs<D, G, W>(job);
 
-    // ---- S^T = K Q^T for 64 keys: lane holds S^T[key 32kb + 8(i/4) + 4hh + i%4][row n]
+    // ---- S^T = K Q^T for 64 keys: lane holds S^T[key 32kb + 8(i/4) + 4hh + i%4][row n].
+    // The 2*NDC matrix instructions alternate the two 32-key blocks (no
+    // back-to-back dependence), K fragments are read KA instructions ahead,
+    // and the staging of tile j+1 into the other buffer (then the loads of
+    // tile j+2) is placed piece by piece between them, so that it issues
+    // while the matrix core runs.  Scheduling barriers keep that order.
+    constexpr int NQK = 2 * C::NDC, KA = 3;
     f32x16 s[2];
+    s[0] = s[1] = (f32x16){};
+    bf16x8 kf[KA];
+    auto kread = [&](int i) {
+      bf16x8 v;
+      __builtin_memcpy(&v, sK + ((i & 1) * 32 + n) * C::KROW + hh * 16 + (i >> 1) * 32, 16);
+      return v;
+    };
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = (f32x16){};
-      const uint8_t* krow = sK + (kb * 32 + n) * C::KROW + hh * 16;
-#pragma unroll
-      for (int c = 0; c < C::NDC; ++c) {
-        bf16x8 kf;
-        __builtin_memcpy(&kf, krow + c * 32, 16);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kb], 0, 0, 0);
+    for (int i = 0; i < KA; ++i) kf[i] = kread(i);
+    TileStager<D, G, W> stager(job, live, smem + ((jt + 1) & 1) * STG, tid);
+    static_for<0, NQK>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % KA], qf[i >> 1], s[i & 1], 0, 0, 0);
+      if constexpr (i + KA < NQK) kf[i % KA] = kread(i + KA);
+      // staging pieces [P0, P1) in this slot
+      constexpr int HP = TileStager<D, G, W>::PIECES;
+      constexpr int P0 = (i * HP + NQK - 1) / NQK, P1 = ((i + 1) * HP + NQK - 1) / NQK;
+      static_for<P0, P1>([&](auto pc) { stager.template piece<decltype(pc)::value>(job); });
+      if constexpr (i == NQK - 1) {
+        // past the last tile this stages and loads unused (clamped) data
+        live = load_jobs<D, G, W>(a, job, tid, jt + 2, page_next, kend_max, hk, page_bad);
+        page_next = lookup_page<D, G, W>(a, tid, jt + 3, kend_max, ptb);
       }
-    }
-
-    // ---- stage tile j+1 (the other buffer was released by the last barrier;
-    // past the last tile this stages unused data), then prefetch tile j+2
-    stage_jobs<D, G, W>(job, live, smem + ((jt + 1) & 1) * STG, tid);
-    live = load_jobs<D, G, W>(a, job, tid, jt + 2, page_next, kend_max, hk);
-    page_next = lookup_page<D, G, W>(a, tid, jt + 3, kend_max, ptb);
+      __builtin_amdgcn_sched_barrier(0);
+    });
 
     // ---- causal mask (diagonal tiles only): key > kend  <=>  offset(i) > lim
     if constexpr (MASK) {
@@ -359,53 +476,157 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     const float m_new = grow ? m_tile : m_run;
     const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
     m_run = m_new;
-    float lsum = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], cscale, -m_new));
-        s[kb][i] = p;
-        lsum += p;
-      }
-    l_run = l_run * alpha + lsum;
+    l_run *= alpha;
     if (__any(grow)) {
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
     }
+    // (a row with no visible key yet keeps -inf: its p must be 0, not NaN)
+    const float m_sub = m_new == -__builtin_inff() ? 0.0f : m_new;
 
-    // ---- P^T operands straight from the accumulators (16-key chunks)
-    bf16x8 pf[4];
+    // ---- P^T operands straight from the accumulators, one 16-key chunk kc
+    // at a time (elements 8(kc&1)..+7 of s[kc/2]), rounded to bf16; the row
+    // sum adds the rounded values (the weights the products use).
+    // O^T += V^T P^T with V^T fragments by transpose reads of the [key][d]
+    // stage: keys 4hh..4hh+3 and 8+4hh..8+4hh+3 of each chunk (the P^T
+    // order).  Chunk 0's exponentials come first; those of chunk kc+1 are
+    // placed between the NDB matrix instructions of chunk kc, V fragments are
+    // read VA instructions ahead.
+    constexpr int NPV = 4 * C::NDB, VA = 3;
+    uint32_t pw[4][4];
+    auto exps = [&](int kc, int j) {  // pair j of chunk kc
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kc >> 1][8 * (kc & 1) + 2 * j], cscale, -m_sub));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kc >> 1][8 * (kc & 1) + 2 * j + 1], cscale, -m_sub));
+      const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnesBf16x2, l_run, false);
+      pw[kc][j] = __builtin_bit_cast(uint32_t, pp);
+    };
+    auto vread = [&](int i) {  // MFMA i: chunk i / NDB, head_dim block i % NDB
+      const uint8_t* vp = vbase + (i / C::NDB) * 16 * C::VROW + (i % C::NDB) * 64;
+      const s16x4 lo = lds_read_tr16(vp);
+      const s16x4 hi = lds_read_tr16(vp + 8 * C::VROW);
+      bf16x8 vf;
+      __builtin_memcpy(&vf, &lo, 8);
+      __builtin_memcpy((char*)&vf + 8, &hi, 8);
+      return vf;
+    };
+    bf16x8 vf[VA];
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
+    for (int i = 0; i < VA; ++i) vf[i] = vread(i);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pf[kc][j] = (__bf16)s[kc >> 1][8 * (kc & 1) + j];
-
-    // ---- O^T += V^T P^T; V^T fragments by transpose reads of the [key][d] stage:
-    // keys 4hh..4hh+3 and 8+4hh..8+4hh+3 of each 16-key chunk (the P^T order)
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const uint8_t* vp = vbase + kc * 16 * C::VROW + db * 64;
-        const s16x4 lo = lds_read_tr16(vp);
-        const s16x4 hi = lds_read_tr16(vp + 8 * C::VROW);
-        bf16x8 vf;
-        __builtin_memcpy(&vf, &lo, 8);
-        __builtin_memcpy((char*)&vf + 8, &hi, 8);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], o[db], 0, 0, 0);
+    for (int j = 0; j < 4; ++j) exps(0, j);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, NPV>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int kc = i / C::NDB, db = i % C::NDB;
+      bf16x8 pf;
+      __builtin_memcpy(&pf, pw[kc], 16);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % VA], pf, o[db], 0, 0, 0);
+      if constexpr (i + VA < NPV) vf[i % VA] = vread(i + VA);
+      if constexpr (kc + 1 < 4) {
+        // pairs [J0, J1) of chunk kc+1 in this slot
+        constexpr int J0 = db * 4 / C::NDB, J1 = (db + 1) * 4 / C::NDB;
+        static_for<J0, J1>([&](auto jc) { exps(kc + 1, decltype(jc)::value); });
       }
-    }
+      __builtin_amdgcn_sched_barrier(0);
+    });
     __syncthreads();  // tile j+1 staged; buffer j&1 free
   };
   // KV tiles entirely at or below the first row's last key need no mask.
   const int n_full = min(ntiles, (kend_min + 1) / C::BN);
-  int jt = 0;
+  int jt = jt_begin;
   for (; jt < n_full; ++jt) tile_step(jt, std::false_type{});
   for (; jt < ntiles; ++jt) tile_step(jt, std::true_type{});
+  if (page_bad) atomicOr(a.err, (uint32_t)NVFP4KV_DEV_PAGE_OOB);
+
+  float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (split >= 0) {
+    // ---- split Q tile: all but the last chunk to arrive publish a partial
+    // (unnormalized O^T, reference max, sum); the last one merges them all in
+    // chunk order (symmetric: the result does not depend on arrival order).
+    // The partials move through device-coherent loads and stores and the
+    // counters through relaxed device-scope atomics: no cache-wide write-back
+    // or invalidate, which would evict the KV tiles other work-groups on the
+    // same L2 are reading.
+    const int sid = split >> 10, chunk = (split >> 5) & 31, nch = split & 31;
+    int* arrive = a.counters + 2 * sid;
+    __shared__ int s_prior;
+    if (tid == 0) s_prior = __hip_atomic_fetch_add(arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int prior = s_prior;
+    const __amdgpu_buffer_rsrc_t parts = coherent_rsrc(
+        a.partials + (int64_t)sid * a.max_chunks * a.partial_floats,
+        (uint32_t)(a.max_chunks * a.partial_floats * 4));
+    const int ml_base = 32 * W * D;  // floats: O^T, then m per row, then l per row
+    if (prior < nch - 1) {
+      const int cb = chunk * (int)a.partial_floats * 4;  // byte offset of this chunk
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+          coherent_store4(parts, cb + ((db * 4 + i4) * C::NT + tid) * 16,
+                          (f32x4){o[db][4 * i4], o[db][4 * i4 + 1], o[db][4 * i4 + 2], o[db][4 * i4 + 3]});
+      if (hh == 0) {
+        coherent_store1(parts, cb + (ml_base + r) * 4, m_run);
+        coherent_store1(parts, cb + (ml_base + 32 * W + r) * 4, l_tot);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial is written
+      __syncthreads();
+      if (tid == 0) __hip_atomic_fetch_add(arrive + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    // last to arrive: the other chunks have all arrived and are finishing
+    // their partials; wait (bounded) until all of them are published
+    if (tid == 0) {
+      int spins = 0;
+      while (__hip_atomic_load(arrive + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nch - 1) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins == (1 << 22)) {
+          atomicOr(a.err, (uint32_t)NVFP4KV_DEV_SPLIT_TIMEOUT);
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    float m_all = m_run;
+    for (int c = 0; c < nch; ++c)
+      if (c != chunk)
+        m_all = __builtin_fmaxf(m_all, coherent_load1(parts, (c * (int)a.partial_floats + ml_base + r) * 4));
+    const float m_ref = m_all == -__builtin_inff() ? 0.0f : m_all;
+    f32x16 acc[C::NDB];
+    float l_acc = 0.0f;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) acc[db] = (f32x16){};
+    // Identical arithmetic for the chunk held in registers and the chunks
+    // read back (explicit FMAs), so the bits do not depend on which chunk
+    // arrived last.
+    for (int c = 0; c < nch; ++c) {
+      const int cb = c * (int)a.partial_floats * 4;
+      const bool mine = c == chunk;
+      const float mc = mine ? m_run : coherent_load1(parts, cb + (ml_base + r) * 4);
+      const float lc = mine ? l_tot : coherent_load1(parts, cb + (ml_base + 32 * W + r) * 4);
+      const float f = __builtin_amdgcn_exp2f(mc - m_ref);
+      l_acc = __builtin_fmaf(lc, f, l_acc);
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          f32x4 v = {o[db][4 * i4], o[db][4 * i4 + 1], o[db][4 * i4 + 2], o[db][4 * i4 + 3]};
+          if (!mine) v = coherent_load4(parts, cb + ((db * 4 + i4) * C::NT + tid) * 16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[db][4 * i4 + e] = __builtin_fmaf(v[e], f, acc[db][4 * i4 + e]);
+        }
+    }
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) o[db] = acc[db];
+    l_tot = l_acc;
+    if (tid == 0) {  // leave the counters zeroed for the next call
+      __hip_atomic_store(arrive, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(arrive + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 
   // ---- epilogue: O / l * g_v -> bf16; lane holds O^T[d][row n]
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = gv / l_tot;
   if (row_valid) {
     uint16_t* orow = a.out + ((int64_t)(q_begin + tok) * a.Hq + hq) * D;
@@ -426,26 +647,40 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-// ---- ragged batches: device-built work list, heaviest tile first.
-// One workgroup: histogram of tile costs (KV tiles a Q tile visits), an
-// exclusive scan in descending cost order, then each request places its
-// tiles (x KV heads) at the next free positions of its cost buckets.
+// ---- device-built work list (ragged or split batches), heaviest item first.
+// One workgroup: histogram of item costs (KV tiles an item visits), an
+// exclusive scan in descending cost order, then each (request, Q tile) pair,
+// one per thread, places its items (x KV heads) at the next free positions of
+// their cost buckets.  An item is a Q tile, or, when split_len > 0, one of
+// the balanced chunks of its KV range.
 constexpr int kCostBuckets = 4096;
+
+__device__ __forceinline__ int tile_cost(int lq, int off, int t, int BQ) {
+  return (off + min((t + 1) * BQ, lq) - 1) / kBlockN + 1;
+}
 
 __global__ __launch_bounds__(1024) void worklist_kernel(const int32_t* __restrict__ qo,
                                                         const int32_t* __restrict__ kvl, int B,
-                                                        int Hk, int BQ, int2* __restrict__ list) {
+                                                        int Hk, int BQ, int QT, int split_len,
+                                                        int4* __restrict__ list) {
   __shared__ int hist[kCostBuckets];
   __shared__ int warp_tot[16];
+  __shared__ int n_split;
   const int tid = threadIdx.x;
   for (int i = tid; i < kCostBuckets; i += 1024) hist[i] = 0;
+  if (tid == 0) n_split = 0;
   __syncthreads();
-  for (int rq = tid; rq < B; rq += 1024) {
+  for (int64_t i = tid; i < (int64_t)B * QT; i += 1024) {
+    const int rq = (int)(i / QT), t = (int)(i - (int64_t)rq * QT);
     const int lq = qo[rq + 1] - qo[rq], off = kvl[rq] - lq;
-    for (int t = 0; t * BQ < lq; ++t) {
-      const int last = off + min((t + 1) * BQ, lq) - 1;
-      const int c = min(last / kBlockN + 1, kCostBuckets - 1);
-      atomicAdd(&hist[c], Hk);
+    if (t * BQ >= lq) continue;
+    {
+      const int c = tile_cost(lq, off, t, BQ);
+      const int nch = split_len > 0 ? (c + split_len - 1) / split_len : 1;
+      for (int k = 0; k < nch; ++k) {
+        const int w = (k + 1) * c / nch - k * c / nch;
+        atomicAdd(&hist[min(w, kCostBuckets - 1)], Hk);
+      }
     }
   }
   __syncthreads();
@@ -475,20 +710,28 @@ __global__ __launch_bounds__(1024) void worklist_kernel(const int32_t* __restric
     run += vals[i];
   }
   __syncthreads();
-  for (int rq = tid; rq < B; rq += 1024) {
+  for (int64_t i = tid; i < (int64_t)B * QT; i += 1024) {
+    const int rq = (int)(i / QT), t = (int)(i - (int64_t)rq * QT);
     const int lq = qo[rq + 1] - qo[rq], off = kvl[rq] - lq;
-    for (int t = 0; t * BQ < lq; ++t) {
-      const int last = off + min((t + 1) * BQ, lq) - 1;
-      const int c = min(last / kBlockN + 1, kCostBuckets - 1);
-      const int p = atomicAdd(&hist[c], Hk);
-      for (int h = 0; h < Hk; ++h) list[p + h] = make_int2(rq, t * Hk + h);
+    if (t * BQ >= lq) continue;
+    {
+      const int c = tile_cost(lq, off, t, BQ);
+      const int nch = split_len > 0 ? (c + split_len - 1) / split_len : 1;
+      const int sid = nch > 1 ? atomicAdd(&n_split, Hk) : -1;
+      for (int k = 0; k < nch; ++k) {
+        const int beg = k * c / nch, end = (k + 1) * c / nch;
+        const int p = atomicAdd(&hist[min(end - beg, kCostBuckets - 1)], Hk);
+        for (int h = 0; h < Hk; ++h)
+          list[p + h] = make_int4(rq, t * Hk + h, (beg << 16) | end,
+                                  nch > 1 ? ((sid + h) << 10) | (k << 5) | nch : -1);
+      }
     }
   }
 }
 
 template <int D, int G, int W>
 void launch_prefill(const PrefillArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((prefill_kernel<D, G, W>), dim3(a.num_tiles), dim3(64 * W), 0, s, a);
+  hipLaunchKernelGGL((prefill_kernel<D, G, W>), dim3(a.num_items), dim3(64 * W), 0, s, a);
 }
 
 }  // namespace
@@ -515,7 +758,7 @@ extern "C" int paged_prefill_causal(const void* q, const int32_t* qo_indptr,
   if (!aligned(q, 16) || !aligned(out, 8) || !aligned(c.k_cache, 16) || !aligned(c.v_cache, 16) ||
       !aligned(c.k_sf, 8) || !aligned(c.v_sf, 8))
     return NVFP4KV_EINVAL;
-  if (p.num_tiles >= (1ll << 31) || p.batch <= 0) return NVFP4KV_EUNSUPPORTED;
+  if (p.num_items >= (1ll << 31) || p.batch <= 0) return NVFP4KV_EUNSUPPORTED;
   if (p.workspace_bytes > 0 && (!workspace || workspace_bytes < p.workspace_bytes ||
                                 !aligned(workspace, 256)))
     return NVFP4KV_EWORKSPACE;
@@ -544,13 +787,20 @@ extern "C" int paged_prefill_causal(const void* q, const int32_t* qo_indptr,
   a.head_first = p.head_first;
   a.nxcd = p.num_xcd > 0 ? p.num_xcd : 1;
   a.num_tiles = (uint32_t)p.num_tiles;
+  a.num_items = (uint32_t)p.num_items;
+  const WorkspaceLayout wl = workspace_layout(p);
   // the heavy/light pairing assumes two co-resident workgroups per CU
   a.snake = p.block_q * (p.num_q_heads / p.num_kv_heads) == 128 &&
             p.num_tiles <= 2 * (int64_t)device_props().cu_count;
-  if (!p.uniform_q) {
-    a.worklist = (const int2*)workspace;
+  if (!p.uniform_q || p.split_len > 0) {
+    a.worklist = (const int4*)workspace;
+    a.counters = (int*)((uint8_t*)workspace + wl.counters);
+    a.partials = (float*)((uint8_t*)workspace + wl.partials);
+    a.partial_floats = wl.partial_bytes / 4;
+    a.max_chunks = p.max_chunks;
     hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(1024), 0, s, qo_indptr, kv_lens, p.batch,
-                       p.num_kv_heads, p.block_q, (int2*)workspace);
+                       p.num_kv_heads, p.block_q, p.q_tiles_per_head, p.split_len,
+                       (int4*)workspace);
   }
   const int G = p.num_q_heads / p.num_kv_heads;
   const int D = p.head_dim;

@@ -96,17 +96,9 @@ def assert_close(got_bf16, ref64, what):
     return float(err.max())
 
 
-def force_tile_waves(K, w, waves):
+def force_tile_waves(K, w, waves, split_len=-1):
     """A plan for w whose attention tiles use `waves` waves of 32 rows (the plan
     picks 4 or 8 by batch size; tests cover both kernels on every shape)."""
-    plan = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), w.num_q_heads,
-                  w.num_kv_heads, w.head_dim, w.page_size, kv_indptr=torch.from_numpy(w.kv_indptr))
-    G = w.num_q_heads // w.num_kv_heads
-    bq = 32 * waves // G
-    st = plan.struct
-    st.block_q = bq
-    st.q_tiles_per_head = (int(w.q_lens.max()) + bq - 1) // bq
-    st.num_tiles = w.num_kv_heads * int(((w.q_lens + bq - 1) // bq).sum())
-    st.workspace_bytes = 0 if st.uniform_q else ((st.num_tiles * 8 + 4096 + 255) // 256) * 256
-    plan._workspace = {}
-    return plan
+    return K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), w.num_q_heads,
+                  w.num_kv_heads, w.head_dim, w.page_size, kv_indptr=torch.from_numpy(w.kv_indptr),
+                  split_len=split_len, tile_waves=waves)

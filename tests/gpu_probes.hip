@@ -4,7 +4,8 @@
 //    [0, +inf] with the hardware conversion and with the software encoder of
 //    nvfp4kv_codec.hpp, and records where the code changes;
 //  * MFMA lane layouts of v_mfma_f32_32x32x16_bf16 / 16x16x32_bf16;
-//  * the FP4 -> bf16 / fp32 hardware conversions with a scale operand.
+//  * the FP4 -> bf16 / fp32 hardware conversions with a scale operand;
+//  * the E4M3 (fp8) -> fp32 pair conversion used to decode block scales.
 #include <hip/hip_runtime.h>
 #include "../nvfp4_paged_kv_amd/csrc/nvfp4kv_codec.hpp"
 
@@ -95,6 +96,23 @@ __global__ void mfma16_kernel(const float* A, const float* B, float* D) {
   for (int r = 0; r < 4; ++r) D[(4 * (l / 16) + r) * 16 + l % 16] = c[r];
 }
 
+// every E4M3 byte b decoded by the pair conversion: thread t < 128 converts the
+// dword holding bytes (2t, 2t+1) in its low half and (2t+1, 2t) in its high
+// half, so both word selects see every byte in both positions
+__global__ void fp8_pairs_kernel(float* out) {
+  const uint32_t t = threadIdx.x;
+  if (t >= 128) return;
+  const uint32_t b0 = 2 * t, b1 = 2 * t + 1;
+  const uint32_t w = b0 | (b1 << 8) | (b1 << 16) | (b0 << 24);
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+  const f2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);
+  out[4 * t + 0] = lo.x;  // byte b0
+  out[4 * t + 1] = lo.y;  // byte b1
+  out[4 * t + 2] = hi.x;  // byte b1
+  out[4 * t + 3] = hi.y;  // byte b0
+}
+
 extern "C" {
 // All pointers are device pointers; every call synchronizes the device.
 int probe_e2m1_scan(uint32_t sign, int mode, uint32_t* count, uint32_t* buf, uint32_t cap) {
@@ -113,6 +131,10 @@ int probe_fp4_to_bf16(const float* scales, int nscale, uint32_t* out_bf16, float
 }
 int probe_mfma32(const float* A, const float* B, float* D) {
   mfma32_kernel<<<1, 64>>>(A, B, D);
+  return hipDeviceSynchronize() == hipSuccess ? 0 : -1;
+}
+int probe_fp8_pairs(float* out) {
+  fp8_pairs_kernel<<<1, 128>>>(out);
   return hipDeviceSynchronize() == hipSuccess ? 0 : -1;
 }
 int probe_mfma16(const float* A, const float* B, float* D) {

@@ -41,6 +41,38 @@ def _plan(K, qo, kv, hq=32, hk=8, d=128, ps=16, **kw):
     return K.plan(torch.as_tensor(qo), torch.as_tensor(kv), hq, hk, d, ps, l2_bytes=32 << 20, **kw)
 
 
+def test_plan_split_workspace_layout(K):
+    """Workspace = work list (16 B per item) + 8 B of counters per split tile
+    + one partial (rows x 128 fp32 O^T + rows fp32 max + rows fp32 sum) per
+    chunk slot; rows = 32 x tile waves."""
+    for waves in (4, 8):
+        p = _plan(K, [0, 2048], [2048], split_len=5, tile_waves=waves)
+        rows = 32 * waves
+        part = rows * 128 * 4 + rows * 8
+        lst = (p.num_items * 16 + 255) // 256 * 256
+        cnt = (lst + p.num_split_tiles * 8 + 255) // 256 * 256
+        assert p.block_q == rows // 4 and p.num_split_tiles > 0
+        assert p.workspace_bytes == cnt + p.num_split_tiles * p.max_chunks * part
+
+
+def _expected_split(qs, kvs, hk, bq, slots, split_len=0):
+    """(split_len, max_chunks, num_items, num_split_tiles) by the documented
+    rule: chunk length = max(total KV tiles / workgroup slots, 8), at least
+    max cost / 16; Q tiles costlier than that are split evenly."""
+    costs = [(kv - q + min((t + 1) * bq, q) - 1) // 64 + 1
+             for q, kv in zip(qs, kvs) for t in range((q + bq - 1) // bq)]
+    ntiles = len(costs) * hk
+    if split_len < 0 or (split_len == 0 and ntiles >= slots) or not costs:
+        return 0, 0, ntiles, 0
+    total = sum(costs) * hk
+    ln = split_len if split_len > 0 else max(-(-total // slots), 8)
+    ln = max(ln, -(-max(costs) // 16))
+    if max(costs) <= ln:
+        return 0, 0, ntiles, 0
+    nch = [-(-c // ln) for c in costs]
+    return ln, -(-max(costs) // ln), sum(nch) * hk, sum(n > 1 for n in nch) * hk
+
+
 @pytest.mark.parametrize("dtype", [torch.int32, torch.uint32])
 @pytest.mark.parametrize("batch", [1, 7, 64, 1024])
 @pytest.mark.parametrize("page_size", [1, 16, 64])
@@ -59,31 +91,61 @@ def test_plan_max_lens(K, dtype, batch, page_size):
     assert p.max_kv_len == int(kv.max())
     assert p.total_q == int(q.sum()) and p.total_kv == int(kv.sum())
     assert p.uniform_q == int(bool((q == q.max()).all()))
-    # head_dim 128: 8-wave tiles (256 rows = 64 tokens x 4 query heads) once
-    # there are at least 4 of them per CU (256 CUs assumed without a device)
-    n8 = 8 * int(((q + 63) // 64).sum())
-    bq = 64 if n8 >= 4 * 256 else 32
+    # head_dim 128: 8-wave tiles (256 rows = 64 tokens x 4 query heads) when
+    # the batch has at least 4 of them per CU (256 CUs), else 4-wave tiles
+    wide = 8 * int(((q + 63) // 64).sum()) >= 4 * 256
+    bq = 64 if wide else 32
     assert p.block_q == bq
     assert p.num_tiles == 8 * int(((q + bq - 1) // bq).sum())
     assert p.max_tile_cost == int(((kv - 1) // 64 + 1)[q > 0].max()) if (q > 0).any() else True
     assert p.kv_bytes == int(kv.sum()) * 8 * (64 + 8) * 2
     assert p.head_first == int(2 * p.kv_bytes <= (32 << 20))
-    assert (p.workspace_bytes == 0) == bool(p.uniform_q)
+    assert (p.workspace_bytes == 0) == (bool(p.uniform_q) and p.split_len == 0)
 
 
 def test_plan_uniform_flags_and_tiles(K):
     p = _plan(K, [0, 1024, 2048], [1024, 1024])
-    assert p.uniform_q == 1 and p.uniform_kv == 1 and p.q_tiles_per_head == 32 and p.num_tiles == 2 * 8 * 32
+    assert p.uniform_q == 1 and p.uniform_kv == 1
+    assert p.block_q == 32 and p.q_tiles_per_head == 32 and p.num_tiles == 2 * 8 * 32
+    # one 2048-token request: 512 4-wave tiles fill the 2 x 256 slots; no split
     p = _plan(K, [0, 2048], [2048])
     assert p.head_first == 1 and p.num_tiles == 8 * 64 and p.block_q == 32
+    assert p.split_len == 0 and p.num_items == p.num_tiles and p.workspace_bytes == 0
+    # forced 8-wave tiles: 256 tiles, one slot each; a forced chunk length of
+    # 17 splits the tiles of cost 18..32 in two
+    q = _plan(K, [0, 2048], [2048], tile_waves=8)
+    assert q.block_q == 64 and q.num_tiles == 256 and q.split_len == 0
+    q = _plan(K, [0, 2048], [2048], tile_waves=8, split_len=17)
+    assert (q.split_len, q.max_chunks, q.num_split_tiles, q.num_items) == (17, 2, 8 * 15, 8 * (17 + 2 * 15))
+    q = _plan(K, [0, 2048], [2048], split_len=4)
+    assert q.split_len == 4 and q.max_chunks == 8
+    q = _plan(K, [0, 2048], [2048], split_len=-1, tile_waves=4)
+    assert q.split_len == 0 and q.workspace_bytes == 0
     p = _plan(K, list(range(0, 1025 * 1024, 1024)), [1024] * 1024)
-    assert p.block_q == 64 and p.num_tiles == 1024 * 8 * 16 and p.head_first == 0
+    assert p.block_q == 64 and p.num_tiles == 1024 * 8 * 16 and p.head_first == 0 and p.split_len == 0
     p = _plan(K, [0, 10, 20], [10, 30])
     assert p.uniform_q == 1 and p.uniform_kv == 0
     p = _plan(K, [0, 10, 25], [10, 30])
     assert p.uniform_q == 0 and p.workspace_bytes >= p.num_tiles * 8
     p = _plan(K, [0, 128, 256], [128, 128], hq=4, hk=2, d=64)
-    assert p.block_q == 64 and p.num_tiles == 8
+    assert p.block_q == 64 and p.num_tiles == 8 and p.split_len == 0
+
+
+@pytest.mark.parametrize("qs,kvs", [([512], [8192]), ([300, 40, 1000], [9000, 40, 3000]),
+                                    ([64] * 3, [20000] * 3), ([2048], [2048])])
+@pytest.mark.parametrize("waves", [0, 4, 8])
+def test_plan_auto_split(K, qs, kvs, waves):
+    """Batches that cannot fill every workgroup slot split their heavy Q
+    tiles' KV ranges (chunked prefill of a short chunk over a long cache)."""
+    qo = [0] + list(np.cumsum(qs))
+    p = _plan(K, qo, kvs, tile_waves=waves)
+    wide = waves == 8 or (waves == 0 and 8 * sum((q + 63) // 64 for q in qs) >= 1024)
+    bq, slots = (64, 256) if wide else (32, 512)
+    assert p.block_q == bq
+    got = (p.split_len, p.max_chunks, p.num_items, p.num_split_tiles)
+    assert got == _expected_split(qs, kvs, 8, bq, slots), got
+    if qs == [512]:
+        assert p.split_len > 0 and p.max_chunks > 1
 
 
 def test_plan_rejects_bad_lengths(K):
@@ -97,6 +159,10 @@ def test_plan_rejects_bad_lengths(K):
         _plan(K, [0, 10], [20], d=96)
     with pytest.raises(K.NVFP4KVError):
         _plan(K, [0, 10], [20], hq=24, hk=8)
+    with pytest.raises(ValueError):
+        _plan(K, [0, 10], [20], tile_waves=6)
+    with pytest.raises(ValueError):
+        _plan(K, [0, 10], [20], hq=4, hk=2, d=64, tile_waves=8)
     p = _plan(K, [0], [])
     assert p.num_tiles == 0
 

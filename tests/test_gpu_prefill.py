@@ -49,13 +49,50 @@ def test_prefill_ragged_small_all_kernels(K, oracle, hq, hk, d):
 
 @pytest.mark.parametrize("hq,hk", [(32, 8), (16, 8), (8, 8), (64, 8)])
 def test_prefill_ragged_small_wide_tiles(K, oracle, hq, hk):
-    """The 8-wave (256-row) kernels on the small ragged batch."""
+    """The 8-wave (256-row) head_dim-128 kernels on the small ragged batch
+    (the plan picks 4-wave tiles for small batches)."""
     banner(f"prefill ragged small, 8-wave tiles, hq={hq} hk={hk}")
     q = [1, 37, 200, 64, 3, 129]
     kv = [1, 37, 333, 700, 3, 130]
     w = W.make_attention(f"ragged_small_wide_{hq}_{hk}", q, kv, hq, hk, 128, 16, 120, seed=14,
                          device="cuda", scales="amax")
     _check(K, oracle, w, plan=force_tile_waves(K, w, 8))
+
+
+@pytest.mark.parametrize("split_len,waves", [(1, 4), (2, 4), (3, 8), (7, 4), (1, 8), (5, 8)])
+def test_prefill_split_kv_chunks(K, oracle, split_len, waves):
+    """Q tiles whose KV range is cut into chunks merged by the last one to
+    finish (forced chunk lengths, including 1-tile chunks where some rows see
+    no key of a chunk), for both tile widths."""
+    banner(f"prefill split KV, chunk length {split_len}, {waves}-wave tiles")
+    q = [1, 37, 200, 64, 3, 129]
+    kv = [1, 37, 333, 700, 3, 130]
+    w = W.make_attention(f"split_{split_len}_{waves}", q, kv, 32, 8, 128, 16, 120, seed=15,
+                         device="cuda", scales="amax")
+    plan = force_tile_waves(K, w, waves, split_len=split_len)
+    assert plan.num_split_tiles > 0
+    _check(K, oracle, w, plan=plan)
+    _check(K, oracle, w, plan=plan)  # the counters were left at zero
+
+
+def test_prefill_split_kv_head_dim_64(K, oracle):
+    banner("prefill split KV, head_dim 64")
+    w = W.make_attention("split_d64", [200, 64, 129], [333, 700, 130], 16, 2, 64, 16, 120, seed=16,
+                         device="cuda", scales="amax")
+    plan = force_tile_waves(K, w, 4, split_len=2)
+    assert plan.num_split_tiles > 0
+    _check(K, oracle, w, plan=plan)
+
+
+def test_prefill_auto_split_short_chunk_long_cache(K, oracle):
+    """A 512-token chunk over an 8192-token cache: too few Q tiles for the
+    GPU, so the plan splits their KV ranges by itself."""
+    banner("prefill 512 over 8192 (automatic split)")
+    w = W.make_attention("chunk_512_8192", [512], [8192], 32, 8, 128, 16, 520, seed=17, device="cuda",
+                         scales="amax")
+    e, out, plan = _check(K, oracle, w)
+    assert plan.split_len > 0 and plan.max_chunks > 1
+    print(f"max err {e:.3g}")
 
 
 def test_prefill_uniform_small_batch(K, oracle):
@@ -69,7 +106,8 @@ def test_prefill_uniform_small_batch(K, oracle):
 
 def test_prefill_2k_full(K, oracle):
     banner("prefill 1x2048 full")
-    e, _, _ = _check(K, oracle, W.prefill_2k("cuda"))
+    e, out, plan = _check(K, oracle, W.prefill_2k("cuda"))
+    assert plan.block_q == 32 and plan.split_len == 0  # 512 4-wave tiles fill the GPU
     print(f"max err {e:.3g}")
 
 
@@ -99,14 +137,17 @@ def test_schedule_orders_give_identical_bits(K):
     banner("schedule order independence")
     w = W.make_attention("order", [256] * 6, [300] * 6, 32, 8, 128, 16, 200, seed=13, device="cuda",
                          scales="amax")
-    base, cache, plan = run_gpu(K, w)
+    base, cache, plan = run_gpu(K, w, plan=K.plan(torch.from_numpy(w.qo_indptr),
+                                                   torch.from_numpy(w.kv_lens), 32, 8, 128, 16,
+                                                   split_len=-1))
     outs = []
     for hf, uq in [(1 - plan.head_first, 1), (plan.head_first, 0)]:
-        p2 = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), 32, 8, 128, 16)
+        p2 = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), 32, 8, 128, 16,
+                    split_len=-1)
         p2.struct.head_first = hf
         if not uq:
             p2.struct.uniform_q = 0
-            p2.struct.workspace_bytes = ((p2.struct.num_tiles * 8 + 4096 + 255) // 256) * 256
+            p2.struct.workspace_bytes = ((p2.struct.num_items * 16 + 255) // 256) * 256
         o, _, _ = run_gpu(K, w, cache=cache, plan=p2)
         outs.append(o)
     for o in outs:

@@ -1,7 +1,8 @@
 """GPU checks of the gfx950 builtins the kernels rely on (probe library
 tests/libnvfp4kv_probes.so): the hardware FP4 conversion used by the append
 against the oracle's E2M1 encoder over every fp32 pattern, the FP4 -> fp32
-decode used by the attention's staging, and the MFMA lane layouts."""
+decode used by the attention's staging, the E4M3 pair decode of its block
+scales, and the MFMA lane layouts."""
 import ctypes
 import os
 
@@ -21,7 +22,8 @@ def probes():
     if not os.path.exists(path):
         pytest.fail("tests/libnvfp4kv_probes.so missing: run __graft_entry__.build()")
     L = ctypes.CDLL(path)
-    for f in ("probe_e2m1_scan", "probe_cvt_pairs", "probe_fp4_to_bf16", "probe_mfma32", "probe_mfma16"):
+    for f in ("probe_e2m1_scan", "probe_cvt_pairs", "probe_fp4_to_bf16", "probe_mfma32", "probe_mfma16",
+              "probe_fp8_pairs"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -89,6 +91,23 @@ def test_fp4_to_f32_decode_and_scaled_forms(probes, oracle):
         bfull = np.array_equal(bfv[i], (grid[byte & 15] * s).astype(np.float32))
         print(f"[probe] scale {s}: f32 form exact product={full}; bf16 form exact product={bfull}; "
               f"sample f32 {f[i, 0x27, :].tolist()} bf16 {bfv[i, 0x27]}", flush=True)
+
+
+def test_e4m3_pair_decode_matches_oracle(probes, oracle):
+    """Every finite E4M3 byte (both signs, subnormals included) decodes to the
+    oracle's value in both halves of the pair and with both word selects."""
+    banner("E4M3 pair decode, all 256 bytes")
+    out = torch.zeros(512, dtype=torch.float32, device="cuda")
+    assert probes.probe_fp8_pairs(P(out)) == 0
+    f = out.cpu().numpy().reshape(128, 4)
+    got = np.empty((256, 2))
+    got[0::2, 0], got[1::2, 0], got[1::2, 1], got[0::2, 1] = f[:, 0], f[:, 1], f[:, 2], f[:, 3]
+    for b in range(256):
+        ref = oracle.e4m3_value(b)
+        if np.isnan(ref):
+            assert np.isnan(got[b]).all(), b
+        else:
+            assert got[b, 0] == ref and got[b, 1] == ref, (b, got[b], ref)
 
 
 def test_mfma_32x32x16_layout(probes):
