@@ -81,7 +81,7 @@ enum {
  *                 positive finite the kernel sets NVFP4KV_DEV_BAD_K_SCALE /
  *                 _BAD_V_SCALE and writes nothing at all.
  *   k_cache, v_cache, k_sf, v_sf  the NHD cache and scale pages (see above);
- *                 k_cache/v_cache 8-byte aligned.  Only the addressed rows
+ *                 k_cache/v_cache 4-byte aligned.  Only the addressed rows
  *                 are written.
  *   dev_error     device uint32 error word (required).
  * Block quantizer (fp32, fixed order): a = max|x_i| (NaN ignored);
