@@ -206,6 +206,54 @@ int paged_prefill_causal(const void* q, const int32_t* qo_indptr, const int32_t*
                          const nvfp4kv_prefill_plan* plan, void* workspace,
                          int64_t workspace_bytes, uint32_t* dev_error, void* stream);
 
+/* Host-side launch plan of one decode batch (filled by nvfp4_decode_plan). */
+typedef struct {
+  int32_t batch, num_q_heads, num_kv_heads, head_dim, page_size;
+  int32_t max_kv_len;       /* decode plan max_kv_len */
+  int64_t total_kv;
+  int32_t chunk_len;        /* keys per KV chunk (a multiple of 64) */
+  int32_t max_chunks;       /* chunks of the longest request */
+  int64_t num_items;        /* waves launched: batch x num_kv_heads x max_chunks */
+  int64_t workspace_bytes;  /* chunk partials (0 when no request has two chunks) */
+} nvfp4kv_decode_plan;
+
+/*
+ * nvfp4_decode_plan -- host-only plan of a decode step: every request has one
+ * new query token (already appended to the cache) that attends to all of its
+ * kv_len keys.  The KV range of a request is cut into chunks of chunk_len
+ * keys, one wave per (request, KV head, chunk), so that short batches still
+ * fill the GPU; the chunks' partial results are merged in chunk order.
+ *   kv_lens_host  int32 [batch], each >= 1.
+ *   chunk_len     keys per chunk: 0 = automatic (at least 256, enough chunks
+ *                 for about 16 waves per CU), else a positive multiple of 64.
+ * Returns NVFP4KV_ERANGE for a kv_len < 1, NVFP4KV_EINVAL for a bad
+ * chunk_len, NVFP4KV_EUNSUPPORTED for shapes paged_prefill_causal does not
+ * support either (head_dim 64 or 128, GQA group 1, 2, 4 or 8).
+ */
+int nvfp4_decode_plan(const int32_t* kv_lens_host, int32_t batch, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                      int32_t chunk_len, nvfp4kv_decode_plan* plan);
+
+/*
+ * paged_decode -- one decode step of attention over the NVFP4 paged cache:
+ * the next step after the prefill, on the same cache, codecs and page table.
+ *   q          bf16 [batch][num_q_heads][head_dim], contiguous, 16-byte aligned.
+ *   kv_indptr, page_table, kv_lens, caches  as for paged_prefill_causal.
+ *   out        bf16 [batch][num_q_heads][head_dim], 8-byte aligned.
+ *   plan       host pointer, from nvfp4_decode_plan for these lengths.
+ *   workspace  device buffer of at least plan->workspace_bytes, 16-byte
+ *              aligned (may be NULL when that is 0); no initial contents are
+ *              needed.  Calls that share a workspace must not overlap.
+ * Semantics: those of paged_prefill_causal with one query row per request
+ * (the row at position kv_len - 1 sees keys 0 .. kv_len - 1).  When a request
+ * has more than one chunk, a second kernel combines the chunks' (unnormalized
+ * O, max, sum) in chunk order.
+ */
+int paged_decode(const void* q, const int32_t* kv_indptr, const int32_t* page_table,
+                 const int32_t* kv_lens, const nvfp4kv_cache* caches, void* out, float sm_scale,
+                 const nvfp4kv_decode_plan* plan, void* workspace, int64_t workspace_bytes,
+                 uint32_t* dev_error, void* stream);
+
 /*
  * nvfp4kv_read_device_error -- the one synchronizing call: waits for `stream`,
  * copies the device error word to *bits_host and, if clear != 0, resets it to

@@ -31,6 +31,7 @@ DEV_BAD_K_SCALE, DEV_BAD_V_SCALE, DEV_SLOT_OOB, DEV_PAGE_OOB, DEV_BAD_SCALE_ATTN
 DEV_SPLIT_TIMEOUT = 32
 
 ENTRY_POINTS = ("nvfp4_append_paged_kv", "nvfp4_prefill_plan", "paged_prefill_causal",
+                "nvfp4_decode_plan", "paged_decode",
                 "nvfp4kv_read_device_error", "nvfp4kv_status_string", "nvfp4kv_abi_version")
 
 
@@ -65,6 +66,16 @@ class PlanStruct(ctypes.Structure):
         return {n: getattr(self, n) for n, _ in self._fields_}
 
 
+class DecodePlanStruct(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("batch", "num_q_heads", "num_kv_heads", "head_dim", "page_size", "max_kv_len")] + \
+               [("total_kv", ctypes.c_int64), ("chunk_len", ctypes.c_int32), ("max_chunks", ctypes.c_int32),
+                ("num_items", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
 _lib = None
 
 
@@ -86,6 +97,11 @@ def lib():
         L.paged_prefill_causal.argtypes = [P, P, P, P, P, ctypes.POINTER(Cache), P, ctypes.c_float,
                                            ctypes.POINTER(PlanStruct), P, I64, P, P]
         L.paged_prefill_causal.restype = ctypes.c_int
+        L.nvfp4_decode_plan.argtypes = [P, I32, I32, I32, I32, I32, I32, ctypes.POINTER(DecodePlanStruct)]
+        L.nvfp4_decode_plan.restype = ctypes.c_int
+        L.paged_decode.argtypes = [P, P, P, P, ctypes.POINTER(Cache), P, ctypes.c_float,
+                                   ctypes.POINTER(DecodePlanStruct), P, I64, P, P]
+        L.paged_decode.restype = ctypes.c_int
         L.nvfp4kv_read_device_error.argtypes = [P, P, ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]
         L.nvfp4kv_read_device_error.restype = ctypes.c_int
         L.nvfp4kv_status_string.argtypes = [ctypes.c_int]
@@ -334,6 +350,64 @@ def paged_prefill_causal(q: torch.Tensor, qo_indptr: torch.Tensor, kv_indptr: to
         _ptr(q), _ptr(qo_indptr), _ptr(kv_indptr), _ptr(page_table), _ptr(kv_lens), ctypes.byref(cs),
         _ptr(out), float(sm_scale), ctypes.byref(plan.struct), _ptr(ws),
         0 if ws is None else ws.numel(), _ptr(err), _stream(dev)), "paged_prefill_causal")
+    return out
+
+
+class DecodePlan:
+    """Host-side plan of one decode step (one query token per request)."""
+
+    def __init__(self, kv_lens, num_q_heads, num_kv_heads, head_dim, page_size, chunk_len: int = 0):
+        kvl = _host_int32(kv_lens, "kv_lens")
+        self.struct = DecodePlanStruct()
+        _check(lib().nvfp4_decode_plan(_ptr(kvl), kvl.numel(), num_q_heads, num_kv_heads, head_dim,
+                                       page_size, chunk_len, ctypes.byref(self.struct)),
+               "nvfp4_decode_plan")
+        self.kv_lens_host = kvl
+        self._workspace = {}
+
+    def __getattr__(self, name):
+        if name == "struct":
+            raise AttributeError(name)
+        return getattr(self.struct, name)
+
+    def workspace(self, device) -> Optional[torch.Tensor]:
+        n = self.struct.workspace_bytes
+        if n == 0:
+            return None
+        device = torch.device(device)
+        if device not in self._workspace:
+            self._workspace[device] = torch.empty(n, dtype=torch.uint8, device=device)
+        return self._workspace[device]
+
+
+def decode_plan(kv_lens, num_q_heads, num_kv_heads, head_dim, page_size, chunk_len: int = 0) -> DecodePlan:
+    """Host plan of one decode step.  chunk_len: keys per KV chunk (0 automatic,
+    else a multiple of 64)."""
+    return DecodePlan(kv_lens, num_q_heads, num_kv_heads, head_dim, page_size, chunk_len)
+
+
+def paged_decode(q: torch.Tensor, kv_indptr: torch.Tensor, page_table: torch.Tensor,
+                 kv_lens: torch.Tensor, caches: PagedCache, out: torch.Tensor, sm_scale: float,
+                 plan: DecodePlan, dev_error: Optional[torch.Tensor] = None):
+    """One decode step over the NVFP4 paged cache.  q/out: bf16 [batch, H_q, D];
+    kv_indptr, page_table, kv_lens: int32 device tensors."""
+    dev = q.device
+    for name, t, dt in (("q", q, torch.bfloat16), ("out", out, torch.bfloat16),
+                        ("kv_indptr", kv_indptr, torch.int32), ("page_table", page_table, torch.int32),
+                        ("kv_lens", kv_lens, torch.int32)):
+        if t.dtype != dt or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor on {dev}")
+    if q.dim() != 3 or out.shape != q.shape or q.shape[2] != caches.head_dim:
+        raise ValueError("q/out must be [batch, num_q_heads, head_dim]")
+    if q.shape[0] != plan.batch or q.shape[1] != plan.num_q_heads:
+        raise ValueError("q does not match the plan")
+    ws = plan.workspace(dev)
+    err = dev_error if dev_error is not None else device_error_word(dev)
+    cs = caches._struct()
+    _check(lib().paged_decode(
+        _ptr(q), _ptr(kv_indptr), _ptr(page_table), _ptr(kv_lens), ctypes.byref(cs), _ptr(out),
+        float(sm_scale), ctypes.byref(plan.struct), _ptr(ws), 0 if ws is None else ws.numel(),
+        _ptr(err), _stream(dev)), "paged_decode")
     return out
 
 

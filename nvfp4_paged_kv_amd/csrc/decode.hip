@@ -1,0 +1,425 @@
+// decode.hip -- one decode step of attention over the NVFP4 paged cache
+// (gfx950, wave64, bf16 MFMA).
+//
+// The step that follows the prefill in serving, on the same cache, codecs and
+// page table: every request has one new query token, already appended, that
+// attends to all of its kv_len keys (the Lq = 1 case of the prefill's
+// bottom-right causal definition).  The KV range of a request is cut into
+// chunks; the chunks' partial results are combined in chunk order by a
+// second kernel, so the result does not depend on scheduling.
+//
+// One wave per (request, KV head, chunk), four independent waves per
+// workgroup, 64-key tiles:
+//  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 contraction
+//    elements, B = Q^T with the G query heads of the KV head as its columns
+//    (columns >= G are zero).  The head_dim contraction runs in a lane-shaped
+//    order: lane (key k, quarter q) supplies, in MFMA c, head_dim elements
+//    q*D/4 + 8c .. +7, and the Q^T operand uses the same order, so each lane
+//    dequantizes one contiguous quarter of its key's code row straight into
+//    registers.  K needs no LDS: each K element feeds one wave only.
+//  * Online softmax per query head in the log2 domain with the prefill's lazy
+//    rescaling; the four lanes of a head (one per quarter) share its max.
+//  * O^T += V^T P^T with v_mfma_f32_16x16x32_bf16: V is dequantized into the
+//    wave's own LDS rows [key][d] and read back with transpose reads in the
+//    key order in which the S^T accumulators hold P^T.
+// E2M1 x E4M3 is exact in bf16; g_k folds into the softmax scale and g_v
+// into the output.
+#include <hip/hip_runtime.h>
+
+#include "nvfp4kv_codec.hpp"
+#include "nvfp4kv_internal.hpp"
+
+namespace nvfp4kv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
+constexpr float kRescaleSlack = 8.0f;  // log2 units, as in the prefill
+constexpr int kWaves = 4;              // independent waves per workgroup
+
+template <int D>
+struct DCfg {
+  static constexpr int NQ = D / 4;         // head_dim elements per lane quarter
+  static constexpr int NC = NQ / 8;        // QK MFMAs per 16-key block (8 elements each)
+  static constexpr int NDB = D / 16;       // 16-row head_dim blocks of O^T
+  static constexpr int VROW = 2 * D + 32;  // padded bf16 V row in LDS (bytes)
+  static constexpr int LDS_WAVE = 64 * VROW;
+};
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const int32_t* kvp;
+  const int32_t* pt;
+  const int32_t* kvl;
+  const uint8_t* kc;
+  const uint8_t* vc;
+  const uint8_t* ksf;
+  const uint8_t* vsf;
+  const float* kscale;
+  const float* vscale;
+  uint16_t* out;
+  float* partials;  // [batch][Hq][max_chunks][D + 4]: O, max, sum
+  uint32_t* err;
+  int64_t num_pages;
+  int64_t num_items;
+  FastDiv ps_div;
+  int Hq, Hk, B;
+  int chunk_len, max_chunks;
+  float sm_scale_log2;
+};
+
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  // lo, hi are exactly representable in bf16: keep their upper halves.
+  return __builtin_amdgcn_perm(f2u(hi), f2u(lo), 0x07060302u);
+}
+
+// One lane's quarter rows of a 64-key tile: for each 16-key block kb, the
+// NQ/2 code bytes of K and of V and their scale bytes (two blocks of 16 for
+// head_dim 128, one for 64).
+template <int D>
+struct Raw {
+  uint32_t k[4][DCfg<D>::NC], v[4][DCfg<D>::NC];
+  uint32_t ksf[4], vsf[4];
+};
+
+// 8 codes (one dword) times the E4M3 scale S, as 8 bf16 values.
+__device__ __forceinline__ bf16x8 dequant8(uint32_t x, float S) {
+  const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 0);
+  const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 1);
+  const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 2);
+  const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 3);
+  const u32x4 w = {bf16_pair(f0[0] * S, f0[1] * S), bf16_pair(f1[0] * S, f1[1] * S),
+                   bf16_pair(f2[0] * S, f2[1] * S), bf16_pair(f3[0] * S, f3[1] * S)};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
+  using C = DCfg<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kWaves * C::LDS_WAVE];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t item = (int64_t)blockIdx.x * kWaves + wave;
+  if (item >= a.num_items) return;
+  // item = ((request * Hk) + kv head) * max_chunks + chunk
+  const int chunk = (int)(item % a.max_chunks);
+  const int64_t bh = item / a.max_chunks;
+  const int hk = (int)(bh % a.Hk), b = (int)(bh / a.Hk);
+  const int Lk = a.kvl[b];
+  const int k0 = chunk * a.chunk_len;
+  if (k0 >= Lk) return;  // (ragged batches: past this request's last chunk)
+  const int k1 = min(Lk, k0 + a.chunk_len);
+  const int ntiles = (k1 - k0 + 63) / 64;
+  const int nchunks = (Lk + a.chunk_len - 1) / a.chunk_len;
+  const int k16 = lane & 15, qq = lane >> 4;  // key within a 16-key block / quarter
+  const int row = lane & 15;                  // query head column of the B and D operands
+  uint8_t* const vst = smem + wave * C::LDS_WAVE;
+  const int32_t* const ptb = a.pt + a.kvp[b];
+
+  const float gk = *a.kscale, gv = *a.vscale;
+  if (item == 0 && lane == 0 && !(scale_ok(gk) && scale_ok(gv)))
+    atomicOr(a.err, (uint32_t)NVFP4KV_DEV_BAD_SCALE_ATTN);
+  const float cscale = a.sm_scale_log2 * gk;
+
+  // ---- Q^T operand: lane (row, qq) holds Q[row][qq*NQ + 8c .. +7] for MFMA c
+  bf16x8 qf[C::NC];
+  {
+    const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + hk * G + min(row, G - 1)) * D + qq * C::NQ;
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) {
+      u32x4 w = *(const u32x4*)(qrow + 8 * c);
+      if (row >= G) w = (u32x4){0u, 0u, 0u, 0u};
+      qf[c] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  // ---- loads: page ids two tiles ahead, NVFP4 bytes one tile ahead.  Keys
+  // past the chunk end are clamped to its last key (valid addresses; masked).
+  bool page_bad = false;
+  auto lookup = [&](int t, int (&pg)[4]) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int key = min(k0 + 64 * t + 16 * kb + k16, k1 - 1);
+      pg[kb] = ptb[fastdiv((uint32_t)key, a.ps_div)];
+    }
+  };
+  auto load = [&](int t, const int (&pg)[4], Raw<D>& r) {
+    const int ps = (int)a.ps_div.d;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int key = min(k0 + 64 * t + 16 * kb + k16, k1 - 1);
+      const bool in_pool = (uint32_t)pg[kb] < (uint64_t)a.num_pages;
+      page_bad |= !in_pool;
+      const int64_t rowi =
+          ((int64_t)(in_pool ? pg[kb] : 0) * ps + (key - (int)fastdiv((uint32_t)key, a.ps_div) * ps)) *
+              a.Hk + hk;
+      const int64_t co = rowi * (D / 2) + qq * (C::NQ / 2);
+      const int64_t so = rowi * (D / 16) + qq * (C::NQ / 16);
+      if constexpr (C::NC == 4) {
+        const u32x4 kw = *(const u32x4*)(a.kc + co), vw = *(const u32x4*)(a.vc + co);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          r.k[kb][c] = kw[c];
+          r.v[kb][c] = vw[c];
+        }
+        r.ksf[kb] = *(const uint16_t*)(a.ksf + so);
+        r.vsf[kb] = *(const uint16_t*)(a.vsf + so);
+      } else {
+        const uint2 kw = *(const uint2*)(a.kc + co), vw = *(const uint2*)(a.vc + co);
+        r.k[kb][0] = kw.x;
+        r.k[kb][1] = kw.y;
+        r.v[kb][0] = vw.x;
+        r.v[kb][1] = vw.y;
+        r.ksf[kb] = a.ksf[so];
+        r.vsf[kb] = a.vsf[so];
+      }
+    }
+  };
+  // the two E4M3 scales of a quarter (head_dim 64: one, used for both halves)
+  auto scales = [&](uint32_t sfw) {
+    const f32x2 s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sfw, 1.0f, false);
+    return C::NC == 4 ? s : (f32x2){s[0], s[0]};
+  };
+
+  f32x4 o[C::NDB];
+#pragma unroll
+  for (int i = 0; i < C::NDB; ++i) o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float m_run = -__builtin_inff(), l_run = 0.0f;
+
+  // V^T transpose-read addressing: lane t of each 16-lane group (quarter qq)
+  // points at 4 consecutive head_dim values of key 4qq + t/4 (+16, +32m).
+  const int voff = (4 * qq + (k16 >> 2)) * C::VROW + 4 * (k16 & 3) * 2;
+
+  Raw<D> raw;
+  int pg[4], pg_next[4];
+  lookup(0, pg);
+  load(0, pg, raw);
+  lookup(1, pg_next);
+
+  for (int t = 0; t < ntiles; ++t) {
+    Raw<D> nraw;
+    load(t + 1, pg_next, nraw);  // past the last tile: clamped, unused
+    lookup(t + 2, pg_next);
+
+    // ---- S^T = K Q^T: s[kb] holds S^T[key 16kb + 4qq + r][head row]
+    f32x4 s[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const f32x2 S = scales(raw.ksf[kb]);
+      s[kb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) {
+        const bf16x8 kf = dequant8(raw.k[kb][c], c < C::NC / 2 ? S[0] : S[1]);
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c], s[kb], 0, 0, 0);
+      }
+    }
+    // ---- stage V (this lane's quarter rows) into the wave's LDS rows
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const f32x2 S = scales(raw.vsf[kb]);
+      uint8_t* vrow = vst + (16 * kb + k16) * C::VROW + qq * C::NQ * 2;
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c)
+        *(bf16x8*)(vrow + 16 * c) = dequant8(raw.v[kb][c], c < C::NC / 2 ? S[0] : S[1]);
+    }
+    // ---- keys past the request's end (last tile only)
+    const int kbase = k0 + 64 * t;
+    if (kbase + 64 > Lk) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (kbase + 16 * kb + 4 * qq + r >= Lk) s[kb][r] = -__builtin_inff();
+    }
+    // ---- online softmax: the head's max over its 4 quarter lanes
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = __builtin_fmaxf(mx, s[kb][r]);
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_tile = mx * cscale;
+    const bool grow = m_tile > m_run + kRescaleSlack;
+    const float m_new = grow ? m_tile : m_run;
+    const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+    m_run = m_new;
+    l_run *= alpha;
+    if (__any(grow)) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
+    }
+    // P^T for the 32 keys of half m: keys 32m + 4qq + r (block 2m), then
+    // 32m + 16 + 4qq + r (block 2m+1); rounded to bf16, the row sum adds the
+    // rounded values
+    bf16x8 pf[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      uint32_t pw[4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r2 = 0; r2 < 2; ++r2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m + h][2 * r2], cscale, -m_new));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m + h][2 * r2 + 1], cscale, -m_new));
+          const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes, l_run, false);
+          pw[2 * h + r2] = __builtin_bit_cast(uint32_t, pp);
+        }
+      __builtin_memcpy(&pf[m], pw, 16);
+    }
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const uint8_t* vp = vst + voff + 32 * m * C::VROW + 16 * db * 2;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 16 * C::VROW));
+        bf16x8 vf;
+        __builtin_memcpy(&vf, &lo, 8);
+        __builtin_memcpy((char*)&vf + 8, &hi, 8);
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[m], o[db], 0, 0, 0);
+      }
+    raw = nraw;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) pg[kb] = pg_next[kb];
+  }
+  if (page_bad) atomicOr(a.err, (uint32_t)NVFP4KV_DEV_PAGE_OOB);
+
+  // ---- the head's sum over its 4 quarter lanes; then output or partial
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (row >= G) return;
+  const int hq = hk * G + row;
+  if (nchunks == 1) {
+    const float inv = gv / l_tot;
+    uint16_t* orow = a.out + ((int64_t)b * a.Hq + hq) * D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const bf16x2 v01 = {(__bf16)(o[db][0] * inv), (__bf16)(o[db][1] * inv)};
+      const bf16x2 v23 = {(__bf16)(o[db][2] * inv), (__bf16)(o[db][3] * inv)};
+      *(uint2*)(orow + 16 * db + 4 * qq) =
+          make_uint2(__builtin_bit_cast(uint32_t, v01), __builtin_bit_cast(uint32_t, v23));
+    }
+  } else {
+    float* part = a.partials + (((int64_t)b * a.Hq + hq) * a.max_chunks + chunk) * decode_partial_floats(D);
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) *(f32x4*)(part + 16 * db + 4 * qq) = o[db];
+    if (qq == 0) {
+      part[D] = m_run;
+      part[D + 1] = l_tot;
+    }
+  }
+}
+
+// Combine the chunks of every request with more than one, in chunk order:
+// one wave per (request, query head), D/64 head_dim elements per lane.
+template <int D>
+__global__ __launch_bounds__(64 * kWaves) void decode_merge_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (item >= (int64_t)a.B * a.Hq) return;
+  const int b = (int)(item / a.Hq);
+  const int n = (a.kvl[b] + a.chunk_len - 1) / a.chunk_len;
+  if (n <= 1) return;
+  constexpr int64_t PF = decode_partial_floats(D);
+  const float* base = a.partials + item * a.max_chunks * PF;
+  float M = -__builtin_inff();
+  for (int c = 0; c < n; ++c) M = __builtin_fmaxf(M, base[c * PF + D]);
+  constexpr int E = D / 64;
+  float acc[E] = {};
+  float L = 0.0f;
+  for (int c = 0; c < n; ++c) {
+    const float f = __builtin_amdgcn_exp2f(base[c * PF + D] - M);
+    L = __builtin_fmaf(base[c * PF + D + 1], f, L);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(base[c * PF + lane * E + e], f, acc[e]);
+  }
+  const float inv = *a.vscale / L;
+  uint16_t* orow = a.out + item * D + lane * E;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const __bf16 v = (__bf16)(acc[e] * inv);
+    orow[e] = __builtin_bit_cast(uint16_t, v);
+  }
+}
+
+template <int D, int G>
+void launch_decode(const DecodeArgs& a, hipStream_t s) {
+  const uint32_t grid = (uint32_t)((a.num_items + kWaves - 1) / kWaves);
+  hipLaunchKernelGGL((decode_kernel<D, G>), dim3(grid), dim3(64 * kWaves), 0, s, a);
+}
+
+}  // namespace
+}  // namespace nvfp4kv
+
+using namespace nvfp4kv;
+
+extern "C" int paged_decode(const void* q, const int32_t* kv_indptr, const int32_t* page_table,
+                            const int32_t* kv_lens, const nvfp4kv_cache* caches, void* out,
+                            float sm_scale, const nvfp4kv_decode_plan* plan, void* workspace,
+                            int64_t workspace_bytes, uint32_t* dev_error, void* stream) {
+  if (!plan || !caches) return NVFP4KV_EINVAL;
+  const nvfp4kv_decode_plan& p = *plan;
+  const nvfp4kv_cache& c = *caches;
+  if (p.num_kv_heads != c.num_kv_heads || p.head_dim != c.head_dim || p.page_size != c.page_size ||
+      p.num_q_heads % p.num_kv_heads != 0)
+    return NVFP4KV_EINVAL;
+  if (p.num_items == 0) return NVFP4KV_OK;
+  if (!q || !kv_indptr || !page_table || !kv_lens || !out || !dev_error || !c.k_cache ||
+      !c.v_cache || !c.k_sf || !c.v_sf || !c.k_scale || !c.v_scale)
+    return NVFP4KV_EINVAL;
+  if (!aligned(q, 16) || !aligned(out, 8) || !aligned(c.k_cache, 16) || !aligned(c.v_cache, 16) ||
+      !aligned(c.k_sf, 8) || !aligned(c.v_sf, 8))
+    return NVFP4KV_EINVAL;
+  if (p.chunk_len <= 0 || p.chunk_len % kBlockN != 0 || p.max_chunks <= 0) return NVFP4KV_EINVAL;
+  if (p.workspace_bytes > 0 &&
+      (!workspace || workspace_bytes < p.workspace_bytes || !aligned(workspace, 16)))
+    return NVFP4KV_EWORKSPACE;
+  DecodeArgs a{};
+  a.q = (const uint16_t*)q;
+  a.kvp = kv_indptr;
+  a.pt = page_table;
+  a.kvl = kv_lens;
+  a.kc = c.k_cache;
+  a.vc = c.v_cache;
+  a.ksf = c.k_sf;
+  a.vsf = c.v_sf;
+  a.kscale = c.k_scale;
+  a.vscale = c.v_scale;
+  a.out = (uint16_t*)out;
+  a.partials = (float*)workspace;
+  a.err = dev_error;
+  a.num_pages = c.num_pages;
+  a.num_items = p.num_items;
+  a.ps_div = make_fastdiv((uint32_t)c.page_size);
+  a.Hq = p.num_q_heads;
+  a.Hk = p.num_kv_heads;
+  a.B = p.batch;
+  a.chunk_len = p.chunk_len;
+  a.max_chunks = p.max_chunks;
+  a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  hipStream_t s = (hipStream_t)stream;
+  const int G = p.num_q_heads / p.num_kv_heads;
+#define NVFP4KV_DCASE(D_, G_) \
+  if (p.head_dim == D_ && G == G_) launch_decode<D_, G_>(a, s); else
+  NVFP4KV_DCASE(128, 1) NVFP4KV_DCASE(128, 2) NVFP4KV_DCASE(128, 4) NVFP4KV_DCASE(128, 8)
+  NVFP4KV_DCASE(64, 1) NVFP4KV_DCASE(64, 2) NVFP4KV_DCASE(64, 4) NVFP4KV_DCASE(64, 8)
+  return NVFP4KV_EUNSUPPORTED;
+#undef NVFP4KV_DCASE
+  if (p.max_chunks > 1) {
+    const uint32_t grid = (uint32_t)(((int64_t)p.batch * p.num_q_heads + kWaves - 1) / kWaves);
+    if (p.head_dim == 128)
+      hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(grid), dim3(64 * kWaves), 0, s, a);
+    else
+      hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(grid), dim3(64 * kWaves), 0, s, a);
+  }
+  return hipGetLastError() == hipSuccess ? NVFP4KV_OK : NVFP4KV_EHIP;
+}

@@ -163,6 +163,52 @@ extern "C" int nvfp4_prefill_plan(const int32_t* qo_indptr_host, const int32_t* 
   return NVFP4KV_OK;
 }
 
+extern "C" int nvfp4_decode_plan(const int32_t* kv_lens_host, int32_t batch, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                 int32_t chunk_len, nvfp4kv_decode_plan* plan) {
+  if (!plan || batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || page_size <= 0 ||
+      head_dim <= 0 || (batch > 0 && !kv_lens_host) || chunk_len < 0 || chunk_len % kBlockN != 0)
+    return NVFP4KV_EINVAL;
+  if (num_q_heads % num_kv_heads != 0) return NVFP4KV_EUNSUPPORTED;
+  const int G = num_q_heads / num_kv_heads;
+  if (!(G == 1 || G == 2 || G == 4 || G == 8)) return NVFP4KV_EUNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return NVFP4KV_EUNSUPPORTED;
+  nvfp4kv_decode_plan p{};
+  p.batch = batch;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.page_size = page_size;
+  int32_t max_kv = 0;
+  int64_t tot_kv = 0;
+  bool bad = false;
+  for (int32_t r = 0; r < batch; ++r) {
+    const int32_t lk = kv_lens_host[r];
+    bad |= lk < 1;
+    max_kv = lk > max_kv ? lk : max_kv;
+    tot_kv += lk;
+  }
+  if (bad) return NVFP4KV_ERANGE;
+  p.max_kv_len = max_kv;
+  p.total_kv = tot_kv;
+  // Chunks: at least kDecodeMinChunk keys (the merge costs one partial per
+  // chunk), and enough of them for about kDecodeWavesPerCu waves per CU.
+  int64_t len = chunk_len;
+  if (len == 0) {
+    const int64_t target = (int64_t)kDecodeWavesPerCu * device_props().cu_count;
+    len = (tot_kv * num_kv_heads + target - 1) / std::max<int64_t>(target, 1);
+    len = std::max<int64_t>((len + kBlockN - 1) / kBlockN * kBlockN, kDecodeMinChunk);
+  }
+  len = std::max<int64_t>(len, ((int64_t)max_kv + kDecodeMaxChunks - 1) / kDecodeMaxChunks);
+  len = (len + kBlockN - 1) / kBlockN * kBlockN;
+  p.chunk_len = (int32_t)std::min<int64_t>(len, 1 << 30);
+  p.max_chunks = batch > 0 ? (int32_t)((max_kv + p.chunk_len - 1) / p.chunk_len) : 0;
+  p.num_items = (int64_t)batch * num_kv_heads * p.max_chunks;
+  p.workspace_bytes = decode_workspace_bytes(p);
+  *plan = p;
+  return NVFP4KV_OK;
+}
+
 extern "C" int nvfp4kv_read_device_error(uint32_t* dev_error, void* stream, uint32_t* bits_host,
                                          int clear) {
   if (!dev_error || !bits_host) return NVFP4KV_EINVAL;

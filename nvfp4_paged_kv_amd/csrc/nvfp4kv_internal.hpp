@@ -48,4 +48,18 @@ inline WorkspaceLayout workspace_layout(const nvfp4kv_prefill_plan& p) {
   return w;
 }
 
+// Decode: chunks of at least kDecodeMinChunk keys, at most kDecodeMaxChunks
+// per request, sized for about kDecodeWavesPerCu waves per CU.  Workspace:
+// one partial of head_dim + 4 fp32 (O, then max and sum; 16-byte rows) per
+// (request, query head, chunk) when some request has two chunks.
+constexpr int kDecodeMinChunk = 256;
+constexpr int kDecodeMaxChunks = 4096;
+constexpr int kDecodeWavesPerCu = 16;
+constexpr int64_t decode_partial_floats(int head_dim) { return head_dim + 4; }
+inline int64_t decode_workspace_bytes(const nvfp4kv_decode_plan& p) {
+  return p.max_chunks > 1 ? (int64_t)p.batch * p.num_q_heads * p.max_chunks *
+                                decode_partial_floats(p.head_dim) * 4
+                          : 0;
+}
+
 }  // namespace nvfp4kv

@@ -167,6 +167,31 @@ def test_plan_rejects_bad_lengths(K):
     assert p.num_tiles == 0
 
 
+def test_decode_plan_chunks_and_workspace(K):
+    """Chunk length: a multiple of 64 and at least 256 keys when automatic (its
+    size also depends on the CU count), or as forced; workspace = one
+    (D + 4)-float partial per (request, query head, chunk) when some request
+    has two chunks."""
+    kv = torch.tensor([1, 300, 4096, 65], dtype=torch.int32)
+    p = K.decode_plan(kv, 32, 8, 128, 16)
+    assert p.chunk_len % 64 == 0 and p.chunk_len >= 256
+    assert p.max_chunks == -(-4096 // p.chunk_len) and p.num_items == 4 * 8 * p.max_chunks
+    assert p.max_kv_len == 4096 and p.total_kv == int(kv.sum())
+    assert p.workspace_bytes == (4 * 32 * p.max_chunks * (128 + 4) * 4 if p.max_chunks > 1 else 0)
+    q = K.decode_plan(kv, 32, 8, 128, 16, chunk_len=128)
+    assert q.chunk_len == 128 and q.max_chunks == 32 and q.num_items == 4 * 8 * 32
+    q = K.decode_plan(torch.tensor([100, 20], dtype=torch.int32), 8, 2, 64, 16, chunk_len=128)
+    assert q.max_chunks == 1 and q.workspace_bytes == 0
+    with pytest.raises(ValueError):
+        K.decode_plan(kv, 32, 8, 128, 16, chunk_len=100)   # not a multiple of 64
+    with pytest.raises(ValueError):
+        K.decode_plan(torch.tensor([5, 0], dtype=torch.int32), 32, 8, 128, 16)  # kv_len < 1
+    with pytest.raises(K.NVFP4KVError):
+        K.decode_plan(kv, 24, 8, 128, 16)                  # GQA group 3
+    p = K.decode_plan(torch.tensor([], dtype=torch.int32), 32, 8, 128, 16)
+    assert p.num_items == 0 and p.workspace_bytes == 0
+
+
 def test_plan_empty_requests(K):
     p = _plan(K, [0, 0, 5], [7, 5])
     assert p.max_q_len == 5 and p.total_q == 5 and p.num_tiles == 8 and p.uniform_q == 0

@@ -209,6 +209,14 @@ def ragged_chunked(device="cpu", batch=256) -> AttentionWorkload:
     return w
 
 
+def decode_batch(device="cpu", batch=32, kv_len=8192) -> AttentionWorkload:
+    """One decode step: 32 requests x 1 new query token over 8192 cached keys
+    each (the token at position kv_len - 1), 32/8 heads, head_dim 128, page
+    16, random page table, scales per-tensor amax / (6*448)."""
+    return make_attention(f"decode_{batch}x{kv_len}_h32_kv8_d128", [1] * batch, [kv_len] * batch,
+                          32, 8, 128, 16, batch * kv_len // 16, seed=5, device=device, scales="amax")
+
+
 def append_stress(device="cpu", tokens=65536) -> AppendWorkload:
     """65536 new tokens, 8 KV heads x head_dim 128, page 16, 32768 pages; slot
     mapping = first T entries of a seeded permutation of all slots; values
@@ -222,7 +230,7 @@ def append_stress(device="cpu", tokens=65536) -> AppendWorkload:
 
 
 ATTENTION_WORKLOADS = {"tiny": tiny, "prefill_2k": prefill_2k, "uniform_batch_1k": uniform_batch_1k,
-                       "ragged_chunked": ragged_chunked}
+                       "ragged_chunked": ragged_chunked, "decode_batch": decode_batch}
 
 
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
