@@ -24,6 +24,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.
 SOURCES = {
     "append.hip": ["-ffp-contract=off"],
     "prefill.hip": [],
+    "decode.hip": [],
     "host.cpp": ["-x", "hip"],
 }
 
@@ -55,6 +56,18 @@ def build(out: str = LIB, defines=()) -> str:
     return out
 
 
+PEAK_LIB = os.path.join(PKG, "libnvfp4kv_peak.so")
+
+
+def build_bench_helpers() -> str:
+    """The achievable-peak probe (an MFMA-only loop) that bench.py loads."""
+    cmd = [_hipcc(), *COMMON, "-shared", os.path.join(CSRC, "peak.hip"), "-o", PEAK_LIB]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"build failed:\n{' '.join(cmd)}\n{r.stderr}")
+    return PEAK_LIB
+
+
 def build_test_helpers() -> None:
     """The GPU probe library and the host build of the codec used by tests/."""
     tests = os.path.join(ROOT, "tests")
@@ -73,3 +86,4 @@ def build_test_helpers() -> None:
 if __name__ == "__main__":
     print(build(defines=sys.argv[1:]))
     build_test_helpers()
+    build_bench_helpers()
