@@ -61,6 +61,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append-stress", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
+    ap.add_argument("--no-achievable", action="store_true",
+                    help="skip the measured achievable peaks (copy, MFMA-only loop)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (HBM-counter calibration)")
     args = ap.parse_args()
@@ -176,9 +179,100 @@ def main():
     del ev
     if not args.no_append_stress:
         result["append_stress"] = bench_append_stress(K, W, dev, torch, np)
+    if not args.no_decode:
+        result["decode"] = bench_decode(K, W, dev, torch, np)
+    if not args.no_achievable:
+        ach = bench_achievable(dev, torch, np)
+        ach["prefill_frac_of_mfma_loop"] = round(pre_tflops / ach["mfma_bf16_TFLOPs"], 4)
+        if "append_stress" in result:
+            ach["append_stress_frac_of_copy"] = round(
+                result["append_stress"]["achieved_GBps"] / ach["copy_GBps"], 4)
+        result["achievable"] = ach
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, flops)
     print(json.dumps(result), flush=True)
+
+
+def bench_decode(K, W, dev, torch, np, iters=12):
+    """One decode step of 32 requests x 8192 cached keys (paged_decode, the
+    plan's automatic chunking), cold like the append stress: median of 12
+    launches, each after the untimed cache-flush read.  Bytes = the NVFP4 K
+    and V codes and scales of every cached key (plus q and out)."""
+    w = W.decode_batch(dev)
+    cache = K.PagedCache.empty(w.num_pages, w.page_size, w.num_kv_heads, w.head_dim, dev,
+                               w.k_scale, w.v_scale)
+    cache.append(w.k, w.v, w.slot_mapping)
+    args = [torch.from_numpy(x).to(dev) for x in (w.kv_indptr, w.page_table, w.kv_lens)]
+    out = torch.empty_like(w.q)
+    plan = K.decode_plan(torch.from_numpy(w.kv_lens), w.num_q_heads, w.num_kv_heads, w.head_dim,
+                         w.page_size)
+    flush = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        K.paged_decode(w.q, *args, cache, out, w.sm_scale, plan)
+    times = []
+    for _ in range(iters):
+        torch.amax(flush)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        K.paged_decode(w.q, *args, cache, out, w.sm_scale, plan)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    bits = K.read_device_error(dev)
+    if bits:
+        raise SystemExit(f"device error bits {bits} in the decode")
+    ms = float(np.median(times))
+    nbytes = (int(w.kv_lens.sum()) * w.num_kv_heads * (w.head_dim // 2 + w.head_dim // 16) * 2
+              + 2 * w.q.numel() * 2)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": w.name, "bound": "hbm", "bytes_per_launch": nbytes,
+            "median_launch_us": round(ms * 1e3, 2), "achieved_GBps": round(gbs, 1),
+            "peak_GBps": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "chunk_len": plan.chunk_len, "cache": "cold (flushed)"}
+
+
+def bench_achievable(dev, torch, np):
+    """Measured achievable peaks on this device: a plain 256 MiB device copy
+    (read + write bytes / time) and the MFMA-only loop of peak.hip (dense
+    v_mfma_f32_32x32x16_bf16, two waves per SIMD); medians of 10 launches,
+    HIP events on the launch stream."""
+    import ctypes
+    from nvfp4_paged_kv_amd.build import PEAK_LIB
+    src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+
+    def timed(fn, n=10):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts))
+
+    copy_s = timed(lambda: dst.copy_(src))
+    out = {"copy_GBps": round(2 * src.numel() / copy_s / 1e9, 1)}
+    if not os.path.exists(PEAK_LIB):
+        raise SystemExit(f"{PEAK_LIB} missing: run __graft_entry__.build()")
+    L = ctypes.CDLL(PEAK_LIB)
+    L.nvfp4kv_mfma_peak_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.nvfp4kv_mfma_peak_probe_flops.restype = ctypes.c_double
+    L.nvfp4kv_mfma_peak_probe_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    blocks, iters = 256 * 4, 2000
+    buf = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def mfma():
+        if L.nvfp4kv_mfma_peak_probe(blocks, iters, ctypes.c_void_p(buf.data_ptr()), stream) != 0:
+            raise SystemExit("MFMA peak probe launch failed")
+
+    mfma_s = timed(mfma)
+    out["mfma_bf16_TFLOPs"] = round(L.nvfp4kv_mfma_peak_probe_flops(blocks, iters) / mfma_s / 1e12, 1)
+    return out
 
 
 def bench_append_stress(K, W, dev, torch, np, iters=12):

@@ -221,11 +221,11 @@ typedef struct {
  * nvfp4_decode_plan -- host-only plan of a decode step: every request has one
  * new query token (already appended to the cache) that attends to all of its
  * kv_len keys.  The KV range of a request is cut into chunks of chunk_len
- * keys, one wave per (request, KV head, chunk), so that short batches still
+ * keys, one wave per (request, chunk, KV head), so that short batches still
  * fill the GPU; the chunks' partial results are merged in chunk order.
  *   kv_lens_host  int32 [batch], each >= 1.
  *   chunk_len     keys per chunk: 0 = automatic (at least 256, enough chunks
- *                 for about 16 waves per CU), else a positive multiple of 64.
+ *                 for about 8 waves per CU), else a positive multiple of 64.
  * Returns NVFP4KV_ERANGE for a kv_len < 1, NVFP4KV_EINVAL for a bad
  * chunk_len, NVFP4KV_EUNSUPPORTED for shapes paged_prefill_causal does not
  * support either (head_dim 64 or 128, GQA group 1, 2, 4 or 8).

@@ -8,8 +8,10 @@
 // chunks; the chunks' partial results are combined in chunk order by a
 // second kernel, so the result does not depend on scheduling.
 //
-// One wave per (request, KV head, chunk), four independent waves per
-// workgroup, 64-key tiles:
+// One wave per (request, KV head, chunk), eight independent waves per
+// workgroup with the KV head fastest: the waves of a workgroup read the
+// different heads' slices of the same token rows together, so each cache line
+// comes from HBM once and serves them all from the CU's caches.  64-key tiles:
 //  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 contraction
 //    elements, B = Q^T with the G query heads of the KV head as its columns
 //    (columns >= G are zero).  The head_dim contraction runs in a lane-shaped
@@ -42,7 +44,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 constexpr float kRescaleSlack = 8.0f;  // log2 units, as in the prefill
-constexpr int kWaves = 4;              // independent waves per workgroup
+constexpr int kWaves = 8;              // independent waves per workgroup
 
 template <int D>
 struct DCfg {
@@ -107,10 +109,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t item = (int64_t)blockIdx.x * kWaves + wave;
   if (item >= a.num_items) return;
-  // item = ((request * Hk) + kv head) * max_chunks + chunk
-  const int chunk = (int)(item % a.max_chunks);
-  const int64_t bh = item / a.max_chunks;
-  const int hk = (int)(bh % a.Hk), b = (int)(bh / a.Hk);
+  // item = ((request * max_chunks) + chunk) * Hk + kv head
+  const int hk = (int)(item % a.Hk);
+  const int64_t bc = item / a.Hk;
+  const int chunk = (int)(bc % a.max_chunks), b = (int)(bc / a.max_chunks);
   const int Lk = a.kvl[b];
   const int k0 = chunk * a.chunk_len;
   if (k0 >= Lk) return;  // (ragged batches: past this request's last chunk)

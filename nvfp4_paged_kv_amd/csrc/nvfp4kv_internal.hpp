@@ -49,12 +49,13 @@ inline WorkspaceLayout workspace_layout(const nvfp4kv_prefill_plan& p) {
 }
 
 // Decode: chunks of at least kDecodeMinChunk keys, at most kDecodeMaxChunks
-// per request, sized for about kDecodeWavesPerCu waves per CU.  Workspace:
+// per request, sized for about kDecodeWavesPerCu waves per CU (one round of
+// the decode kernel's 8-wave workgroups, one per CU).  Workspace:
 // one partial of head_dim + 4 fp32 (O, then max and sum; 16-byte rows) per
 // (request, query head, chunk) when some request has two chunks.
 constexpr int kDecodeMinChunk = 256;
 constexpr int kDecodeMaxChunks = 4096;
-constexpr int kDecodeWavesPerCu = 16;
+constexpr int kDecodeWavesPerCu = 8;
 constexpr int64_t decode_partial_floats(int head_dim) { return head_dim + 4; }
 inline int64_t decode_workspace_bytes(const nvfp4kv_decode_plan& p) {
   return p.max_chunks > 1 ? (int64_t)p.batch * p.num_q_heads * p.max_chunks *
