@@ -35,7 +35,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("prefill.hip", "append.hip", "nvfp4kv_codec.hpp"):
+    for f in ("prefill.hip", "append.hip", "decode.hip", "nvfp4kv_codec.hpp"):
         h.update(open(os.path.join(ROOT, "nvfp4_paged_kv_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -142,11 +142,7 @@ def main():
     pre_tflops = flops / (pre_ms * 1e-3) / 1e12
     G = w.num_q_heads // w.num_kv_heads
     kernel_name = f"prefill_kernel<{w.head_dim},{G},{plan.block_q * G // 32}>"
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        t = json.load(open(TRAFFIC_FILE))
-        if t.get("kernel_source_hash") == kernel_source_hash():
-            traffic = t.get("prefill_2k", {}).get("bytes_per_launch")
+    traffic = _traffic("prefill_2k")
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -193,6 +189,16 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def _traffic(key):
+    """HBM bytes per launch of one profiled kernel (profiles/traffic.json),
+    or None when the kernel sources changed since the counters were taken."""
+    if os.path.exists(TRAFFIC_FILE):
+        t = json.load(open(TRAFFIC_FILE))
+        if t.get("kernel_source_hash") == kernel_source_hash():
+            return t.get(key, {}).get("bytes_per_launch")
+    return None
+
+
 def bench_decode(K, W, dev, torch, np, iters=12):
     """One decode step of 32 requests x 8192 cached keys (paged_decode, the
     plan's automatic chunking), cold like the append stress: median of 12
@@ -228,7 +234,7 @@ def bench_decode(K, W, dev, torch, np, iters=12):
     return {"workload": w.name, "bound": "hbm", "bytes_per_launch": nbytes,
             "median_launch_us": round(ms * 1e3, 2), "achieved_GBps": round(gbs, 1),
             "peak_GBps": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "chunk_len": plan.chunk_len, "cache": "cold (flushed)"}
+            "chunk_len": plan.chunk_len, "cache": "cold (flushed)", "traffic": _traffic("decode")}
 
 
 def bench_achievable(dev, torch, np):
@@ -300,7 +306,8 @@ def bench_append_stress(K, W, dev, torch, np, iters=12):
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"workload": a.name, "bound": "hbm", "bytes_per_launch": nbytes,
             "median_launch_us": round(ms * 1e3, 2), "achieved_GBps": round(gbs, 1),
-            "peak_GBps": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4), "cache": "cold (flushed)"}
+            "peak_GBps": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4), "cache": "cold (flushed)",
+            "traffic": _traffic("append_stress")}
 
 
 def cpu_baseline(w, flops_full, hk_s=8):

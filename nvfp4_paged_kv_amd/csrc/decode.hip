@@ -332,17 +332,38 @@ __global__ __launch_bounds__(64 * kWaves) void decode_merge_kernel(DecodeArgs a)
   const int n = (a.kvl[b] + a.chunk_len - 1) / a.chunk_len;
   if (n <= 1) return;
   constexpr int64_t PF = decode_partial_floats(D);
+  constexpr int U = 8;  // chunks whose loads are issued together
   const float* base = a.partials + item * a.max_chunks * PF;
   float M = -__builtin_inff();
-  for (int c = 0; c < n; ++c) M = __builtin_fmaxf(M, base[c * PF + D]);
+  for (int c0 = 0; c0 < n; c0 += U) {
+    float mc[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) mc[i] = c0 + i < n ? base[(c0 + i) * PF + D] : -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < U; ++i) M = __builtin_fmaxf(M, mc[i]);
+  }
   constexpr int E = D / 64;
   float acc[E] = {};
   float L = 0.0f;
-  for (int c = 0; c < n; ++c) {
-    const float f = __builtin_amdgcn_exp2f(base[c * PF + D] - M);
-    L = __builtin_fmaf(base[c * PF + D + 1], f, L);
+  for (int c0 = 0; c0 < n; c0 += U) {
+    float mc[U], lc[U], oc[U][E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(base[c * PF + lane * E + e], f, acc[e]);
+    for (int i = 0; i < U; ++i) {
+      const int c = min(c0 + i, n - 1);  // past the end: a valid chunk, weight 0
+      mc[i] = c0 + i < n ? base[c * PF + D] : -__builtin_inff();
+      lc[i] = base[c * PF + D + 1];
+#pragma unroll
+      for (int e = 0; e < E; ++e) oc[i][e] = base[c * PF + lane * E + e];
+    }
+    // in chunk order: the same sums whatever the loads' timing
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      if (c0 + i >= n) break;
+      const float f = __builtin_amdgcn_exp2f(mc[i] - M);
+      L = __builtin_fmaf(lc[i], f, L);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(oc[i][e], f, acc[e]);
+    }
   }
   const float inv = *a.vscale / L;
   uint16_t* orow = a.out + item * D + lane * E;
