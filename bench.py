@@ -170,6 +170,7 @@ def main():
                    "achieved_GBps": round(abytes / (app_ms * 1e-3) / 1e9, 1), "peak_GBps": HBM_PEAK_GBS,
                    "frac": round(abytes / (app_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "plan_host_us": round(plan_us, 2),
+        "plan_bench": bench_plan(K, torch, np),
         "kernel_source_hash": kernel_source_hash(),
     }
     del ev
@@ -187,6 +188,53 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, flops)
     print(json.dumps(result), flush=True)
+
+
+def bench_plan(K, torch, np, batches=(64, 256, 1024), reps=50):
+    """Host time of the plan step on ragged batches of B requests (q_len
+    U{1..512}, kv_len = q_len + U{0..3584}, seeded): the library's plan call
+    (length checks, maxima, totals, tile counts, chunk split) through the
+    binding, against two ways of taking only its first part (max q/kv length,
+    totals, the q_len <= kv_len check) in Python: a loop over the requests
+    reading one tensor element at a time, and whole-tensor reductions."""
+    res = {}
+    for B in batches:
+        rng = np.random.default_rng(1000 + B)
+        ql = rng.integers(1, 513, B).astype(np.int32)
+        kvl = (ql + rng.integers(0, 3585, B)).astype(np.int32)
+        qo = torch.from_numpy(np.concatenate([[0], np.cumsum(ql)]).astype(np.int32))
+        kv = torch.from_numpy(kvl)
+
+        def native():
+            return K.plan(qo, kv, 32, 8, 128, 16)
+
+        def loop():
+            mq = mk = tq = tk = 0
+            for i in range(B):
+                a, b = int(qo[i + 1]) - int(qo[i]), int(kv[i])
+                if a > b:
+                    raise ValueError("q_len > kv_len")
+                mq, mk, tq, tk = max(mq, a), max(mk, b), tq + a, tk + b
+            return mq, mk, tq, tk
+
+        def vectorised():
+            d = qo[1:] - qo[:-1]
+            if bool((d > kv).any()):
+                raise ValueError("q_len > kv_len")
+            return int(d.max()), int(kv.max()), int(qo[-1]), int(kv.sum())
+
+        p = native()
+        assert (p.max_q_len, p.max_kv_len, p.total_q, p.total_kv) == loop() == vectorised()
+        row = {}
+        for name, fn, n in (("native_us", native, reps), ("python_loop_us", loop, max(3, reps // 10)),
+                            ("torch_vectorised_us", vectorised, reps)):
+            fn()
+            t0 = time.perf_counter()
+            for _ in range(n):
+                fn()
+            row[name] = round((time.perf_counter() - t0) / n * 1e6, 2)
+        res[str(B)] = row
+    return res
 
 
 def _traffic(key):

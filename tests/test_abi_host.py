@@ -252,3 +252,11 @@ def test_fastdiv(host_codec):
     for d in [1, 2, 3, 7, 8, 16, 17, 64, 100, 1000, 65535, 65536, 123457, 2**31 - 1]:
         host_codec.host_fastdiv(_p(n), ctypes.c_int64(n.size), ctypes.c_uint32(d), _p(q))
         assert np.array_equal(q, n // np.uint32(d)), d
+
+
+def test_plan_bench_paths_agree(K):
+    """The plan micro-benchmark's three paths compute the same maxima and
+    totals on a seeded ragged batch (the benchmark asserts it before timing)."""
+    import bench
+    res = bench.bench_plan(K, torch, np, batches=(64,), reps=2)
+    assert set(res["64"]) == {"native_us", "python_loop_us", "torch_vectorised_us"}

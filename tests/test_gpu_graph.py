@@ -1,0 +1,95 @@
+"""The whole step captured into one HIP graph (through torch.cuda.graph) and
+replayed: append of the batch's K/V rows, the causal prefill (with split Q
+tiles, so the merge counters must come back to zero between replays) and the
+decode step (several chunks, so the merge kernel runs too).  Every replay
+follows fresh inputs written by ordinary eager copies, and its outputs must
+equal, bit for bit, the same calls made eagerly on the same inputs; the eager
+results themselves are held to the oracle by the other GPU tests, and once
+here on the first inputs."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_helpers import assert_close, banner, gpu_cache, oracle_outputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    import nvfp4_paged_kv_amd as K
+    K.lib()
+    return K
+
+
+def _fresh(shape, seed, stream):
+    return W.normal_bf16(shape, seed, stream, "cuda")
+
+
+def test_graph_replays_match_eager(K, oracle):
+    banner("graph capture of append + prefill + decode, 4 replays")
+    q_lens = [96, 300, 1, 517]
+    kv_lens = [200, 300, 700, 1100]
+    w = W.make_attention("graph_step", q_lens, kv_lens, 16, 4, 128, 16, 160, seed=31, device="cuda",
+                         scales="amax")
+    dev = "cuda"
+    cache = gpu_cache(K, w)
+    qo, kvp, pt, kvl = (torch.from_numpy(x).to(dev) for x in (w.qo_indptr, w.kv_indptr,
+                                                               w.page_table, w.kv_lens))
+    pplan = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), w.num_q_heads,
+                   w.num_kv_heads, w.head_dim, w.page_size, kv_indptr=torch.from_numpy(w.kv_indptr),
+                   split_len=3)
+    assert pplan.num_split_tiles > 0
+    dplan = K.decode_plan(torch.from_numpy(w.kv_lens), w.num_q_heads, w.num_kv_heads, w.head_dim,
+                          w.page_size, chunk_len=128)
+    assert dplan.max_chunks > 1
+    # static inputs and outputs of the captured step
+    k, v, q = w.k.clone(), w.v.clone(), w.q.clone()
+    qd = _fresh((w.batch, w.num_q_heads, w.head_dim), 31, 7)
+    out_p = torch.empty_like(q)
+    out_d = torch.empty_like(qd)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def step(out_prefill, out_decode):
+        cache.append(k, v, w.slot_mapping, dev_error=err)
+        K.paged_prefill_causal(q, qo, kvp, pt, kvl, cache, out_prefill, w.sm_scale, plan=pplan,
+                               dev_error=err)
+        K.paged_decode(qd, kvp, pt, kvl, cache, out_decode, w.sm_scale, dplan, dev_error=err)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside capture (workspaces allocated here)
+        step(out_p, out_d)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(out_p, out_d)
+    torch.cuda.synchronize()
+
+    eager_p, eager_d = torch.empty_like(out_p), torch.empty_like(out_d)
+    prev = None
+    for r in range(4):
+        if r > 0:  # new inputs through eager copies between replays
+            k.copy_(_fresh(k.shape, 40 + r, 1))
+            v.copy_(_fresh(v.shape, 40 + r, 2))
+            q.copy_(_fresh(q.shape, 40 + r, 0))
+            qd.copy_(_fresh(qd.shape, 40 + r, 7))
+        out_p.fill_(0)
+        out_d.fill_(0)
+        graph.replay()
+        torch.cuda.synchronize()
+        got_p, got_d = out_p.clone(), out_d.clone()
+        step(eager_p, eager_d)
+        torch.cuda.synchronize()
+        assert K.read_device_error(word=err) == 0
+        assert torch.equal(got_p.view(torch.int16), eager_p.view(torch.int16)), f"replay {r}: prefill"
+        assert torch.equal(got_d.view(torch.int16), eager_d.view(torch.int16)), f"replay {r}: decode"
+        if prev is not None:
+            assert not torch.equal(got_p, prev), "replay produced the previous outputs"
+        prev = got_p
+        if r == 0:
+            ref, rows = oracle_outputs(oracle, w)
+            assert_close(got_p.index_select(0, torch.from_numpy(rows).cuda()), ref, w.name)
+        print(f"replay {r}: bit-identical to eager", flush=True)
