@@ -10,8 +10,9 @@ reported separately.
 
 Prints one JSON line.  `value` is causal-prefill TFLOP/s over the whole step
 (algorithmic flops 4 * head_dim * allowed (query, key) pairs per query head,
-divided by the step time).  Also reported: per-kernel times from HIP events
-on the launch stream, the roofline of the dominant kernel, the append's
+divided by the step time).  Also reported: per-kernel launch durations
+(HIP events on the launch stream around replays of a graph of back-to-back
+launches of that kernel), the roofline of the dominant kernel, the append's
 achieved GB/s on this workload and on the 65,536-token append stress
 workload, and the CPU oracle timed on a bounded sample.
 
@@ -57,8 +58,10 @@ def append_bytes(tokens, heads, d):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    # the clocks settle after ~30-40 ms of sustained launches; 1000 warm-up
+    # steps (~60 ms) reach the steady state the timed steps measure
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append-stress", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
@@ -124,17 +127,13 @@ def main():
     if bits:
         raise SystemExit(f"device error bits {bits}")
 
-    # per-kernel durations: HIP events on the launch stream (torch's current stream)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for e in ev:
-        e[0].record()
-        cache.append(w.k, w.v, w.slot_mapping)
-        e[1].record()
-        K.paged_prefill_causal(w.q, qo_d, kvp_d, pt_d, kvl_d, cache, out, w.sm_scale, plan=plan)
-        e[2].record()
-    torch.cuda.synchronize()
-    app_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
-    pre_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    # per-kernel launch durations: each kernel's launches captured back to back
+    # into a graph and replayed between two HIP events on the launch stream
+    # (torch's current stream), so that host-side launch cost does not pace
+    # the short append kernel
+    app_ms = graph_launch_ms(torch, lambda: cache.append(w.k, w.v, w.slot_mapping))
+    pre_ms = graph_launch_ms(torch, lambda: K.paged_prefill_causal(w.q, qo_d, kvp_d, pt_d, kvl_d, cache,
+                                                                   out, w.sm_scale, plan=plan))
 
     flops = attention_flops(w.q_lens, w.kv_lens, w.num_q_heads, w.head_dim)
     abytes = append_bytes(int(w.kv_lens.sum()), w.num_kv_heads, w.head_dim)
@@ -173,7 +172,6 @@ def main():
         "plan_bench": bench_plan(K, torch, np),
         "kernel_source_hash": kernel_source_hash(),
     }
-    del ev
     if not args.no_append_stress:
         result["append_stress"] = bench_append_stress(K, W, dev, torch, np)
     if not args.no_decode:
@@ -188,6 +186,30 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, flops)
     print(json.dumps(result), flush=True)
+
+
+def graph_launch_ms(torch, fn, per_graph=50, replays=20):
+    """Average duration (ms) of one launch of `fn`: `per_graph` launches
+    captured into one graph, replayed `replays` times between two events."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(per_graph):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) / (per_graph * replays)
 
 
 def bench_plan(K, torch, np, batches=(64, 256, 1024), reps=50):
