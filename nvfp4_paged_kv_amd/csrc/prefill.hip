@@ -171,42 +171,78 @@ __device__ __forceinline__ int job_key(int tid) {
 // clamped to the last key any row sees; ids outside the pool read page 0),
 // and what is loaded is only inspected one step later: no branch or select
 // forces a wait on a load that is meant to stay in flight during a tile.
-
-// Raw page id of this thread's key in KV tile jt.
-template <int D, int G, int W>
-__device__ __forceinline__ int lookup_page(const PrefillArgs& a, int tid, int jt, int kend_max,
-                                           const int32_t* ptb) {
-  const int kk = min(jt * Cfg<D, G, W>::BN + job_key<D, G, W>(tid), kend_max);
-  return ptb[fastdiv((uint32_t)kk, a.ps_div)];
-}
-
-// Issue the loads of this thread's jobs of KV tile jt; returns whether the
-// key is live (at or before the last key any row sees, in a valid page) and
-// notes in page_bad a live key whose page id is outside the pool.
-template <int D, int G, int W>
-__device__ __forceinline__ bool load_jobs(const PrefillArgs& a, RawJob<D> (&job)[Cfg<D, G, W>::JOBS_PER_THREAD],
-                                          int tid, int jt, int page, int kend_max, int hk,
-                                          bool& page_bad) {
+//
+// Where this thread's key of KV tile jt lives.  With PA (the page size
+// divides the 64-key tile, so it is a power of two up to 64) the key keeps
+// its page slot and in-page row in every tile: the tile's page is entry
+// jt * (64 / ps) + key / ps of the request's page list, and each load address
+// is one multiply-add from a per-job base.  Otherwise the page and the row
+// in it come from a division of the key's position.
+template <int D, int G, int W, bool PA>
+struct KeyAddr {
   using C = Cfg<D, G, W>;
-  const int kk = jt * C::BN + job_key<D, G, W>(tid);
-  const bool live = kk <= kend_max;  // later keys are masked for every row: zeros
-  const bool in_pool = (uint32_t)page < (uint64_t)a.num_pages;
-  page_bad |= live && !in_pool;  // reported once, after the KV loop
-  const int ps = (int)a.ps_div.d;
-  const int64_t row =
-      ((int64_t)(in_pool ? page : 0) * ps + (kk - (int)fastdiv((uint32_t)kk, a.ps_div) * ps)) * a.Hk + hk;
+  const uint8_t* code0[C::JOBS_PER_THREAD];  // job j's codes in page 0 (PA: at this key's row)
+  const uint8_t* sf0[C::JOBS_PER_THREAD];    // its scale row likewise
+  const int32_t* ptb;                        // the request's page list
+  uint32_t page_code_bytes, page_sf_bytes;   // one page of codes / scales (PA)
+  int key, kend_max, tpg, kq, kmaxq;
+
+  __device__ __forceinline__ KeyAddr(const PrefillArgs& a, int tid, int hk, int kend_max_,
+                                     const int32_t* ptb_)
+      : ptb(ptb_), kend_max(kend_max_) {
+    key = job_key<D, G, W>(tid);
+    const int ps = (int)a.ps_div.d;
+    const int row0 = PA ? (key & (ps - 1)) * a.Hk + hk : hk;  // (token, head) row within page 0
 #pragma unroll
-  for (int j = 0; j < C::JOBS_PER_THREAD; ++j) {
-    const int id = tid + C::NT * j;
-    const int tensor = id / (C::BN * C::PARTS);  // 0: K, 1: V
-    const int part = id % C::PARTS;
-    const uint8_t* cb = tensor ? a.vc : a.kc;
-    const uint8_t* sb = tensor ? a.vsf : a.ksf;
-    job[j].pk = *(const u32x4*)(cb + row * (D / 2) + part * 16);
-    job[j].sfrow = *(const decltype(job[j].sfrow)*)(sb + row * (D / 16));
+    for (int j = 0; j < C::JOBS_PER_THREAD; ++j) {
+      const int id = tid + C::NT * j;
+      const int tensor = id / (C::BN * C::PARTS);  // 0: K, 1: V
+      const int part = id % C::PARTS;
+      code0[j] = (tensor ? a.vc : a.kc) + (int64_t)row0 * (D / 2) + part * 16;
+      sf0[j] = (tensor ? a.vsf : a.ksf) + (int64_t)row0 * (D / 16);
+    }
+    tpg = kq = kmaxq = 0;
+    page_code_bytes = page_sf_bytes = 0;
+    if constexpr (PA) {
+      tpg = C::BN / ps;
+      kq = key / ps;
+      kmaxq = kend_max / ps;
+      page_code_bytes = (uint32_t)(ps * a.Hk * (D / 2));
+      page_sf_bytes = (uint32_t)(ps * a.Hk * (D / 16));
+    }
   }
-  return live && in_pool;
-}
+
+  // raw page id of the key in KV tile jt (clamped to the last key any row sees)
+  __device__ __forceinline__ int lookup(const PrefillArgs& a, int jt) const {
+    if constexpr (PA) return ptb[min(jt * tpg + kq, kmaxq)];
+    else return ptb[fastdiv((uint32_t)min(jt * C::BN + key, kend_max), a.ps_div)];
+  }
+
+  // Issue the loads of the thread's jobs of KV tile jt; returns whether the
+  // key is live (at or before the last key any row sees, in a valid page) and
+  // notes in page_bad a live key whose page id is outside the pool.
+  __device__ __forceinline__ bool load(const PrefillArgs& a, RawJob<D>* job, int jt, int page,
+                                       bool& page_bad) const {
+    const int kk = jt * C::BN + key;
+    const bool live = kk <= kend_max;  // later keys are masked for every row: zeros
+    const bool in_pool = (uint32_t)page < (uint64_t)a.num_pages;
+    page_bad |= live && !in_pool;  // reported once, after the KV loop
+    const uint32_t pg = in_pool ? (uint32_t)page : 0u;
+#pragma unroll
+    for (int j = 0; j < C::JOBS_PER_THREAD; ++j) {
+      if constexpr (PA) {
+        job[j].pk = *(const u32x4*)(code0[j] + (uint64_t)pg * page_code_bytes);
+        job[j].sfrow = *(const decltype(job[j].sfrow)*)(sf0[j] + (uint64_t)pg * page_sf_bytes);
+      } else {
+        const int ps = (int)a.ps_div.d;
+        const int64_t rows = ((int64_t)pg * ps + (kk - (int)fastdiv((uint32_t)kk, a.ps_div) * ps)) * a.Hk;
+        job[j].pk = *(const u32x4*)(code0[j] + rows * (D / 2));
+        job[j].sfrow = *(const decltype(job[j].sfrow)*)(sf0[j] + rows * (D / 16));
+      }
+    }
+    return live && in_pool;
+  }
+};
 
 // Pin the first use of the prefetched registers at the point of the call
 // (right after a barrier): otherwise the compiler hoists their unpacking into
@@ -295,7 +331,7 @@ struct TileStager {
   }
 };
 
-template <int D, int G, int W>
+template <int D, int G, int W, bool PA>
 __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   using C = Cfg<D, G, W>;
   // Two staging buffers: tile j+1 is dequantized into one while tile j is
@@ -359,9 +395,9 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   // flight while tile jt is computed.
   RawJob<D> job[C::JOBS_PER_THREAD];
   bool page_bad = false;
-  bool live = load_jobs<D, G, W>(a, job, tid, jt_begin, lookup_page<D, G, W>(a, tid, jt_begin, kend_max, ptb),
-                                 kend_max, hk, page_bad);
-  int page_next = lookup_page<D, G, W>(a, tid, jt_begin + 1, kend_max, ptb);
+  const KeyAddr<D, G, W, PA> ka(a, tid, hk, kend_max, ptb);
+  bool live = ka.load(a, job, jt_begin, ka.lookup(a, jt_begin), page_bad);
+  int page_next = ka.lookup(a, jt_begin + 1);
 
   const int r = wave * 32 + n;  // this lane's tile row
   const int tr = r % C::BQ, g = r / C::BQ;
@@ -405,8 +441,8 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   // next tile's NVFP4 bytes and the one after's page ids in flight.
   pin_jobs<D, G, W>(job);
   stage_jobs<D, G, W>(job, live, smem + (jt_begin & 1) * STG, tid);
-  live = load_jobs<D, G, W>(a, job, tid, jt_begin + 1, page_next, kend_max, hk, page_bad);
-  page_next = lookup_page<D, G, W>(a, tid, jt_begin + 2, kend_max, ptb);
+  live = ka.load(a, job, jt_begin + 1, page_next, page_bad);
+  page_next = ka.lookup(a, jt_begin + 2);
   __syncthreads();
 
   // One KV tile j: S^T = K Q^T from buffer j&1; dequantize tile j+1 into the
@@ -446,8 +482,8 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
       static_for<P0, P1>([&](auto pc) { stager.template piece<decltype(pc)::value>(job); });
       if constexpr (i == NQK - 1) {
         // past the last tile this stages and loads unused (clamped) data
-        live = load_jobs<D, G, W>(a, job, tid, jt + 2, page_next, kend_max, hk, page_bad);
-        page_next = lookup_page<D, G, W>(a, tid, jt + 3, kend_max, ptb);
+        live = ka.load(a, job, jt + 2, page_next, page_bad);
+        page_next = ka.lookup(a, jt + 3);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -731,7 +767,10 @@ __global__ __launch_bounds__(1024) void worklist_kernel(const int32_t* __restric
 
 template <int D, int G, int W>
 void launch_prefill(const PrefillArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((prefill_kernel<D, G, W>), dim3(a.num_items), dim3(64 * W), 0, s, a);
+  if (kBlockN % a.ps_div.d == 0)
+    hipLaunchKernelGGL((prefill_kernel<D, G, W, true>), dim3(a.num_items), dim3(64 * W), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, G, W, false>), dim3(a.num_items), dim3(64 * W), 0, s, a);
 }
 
 }  // namespace

@@ -47,6 +47,21 @@ def test_prefill_ragged_small_all_kernels(K, oracle, hq, hk, d):
     _check(K, oracle, w)
 
 
+@pytest.mark.parametrize("ps,d,waves", [(1, 128, 4), (8, 64, 4), (32, 128, 8), (64, 128, 4),
+                                         (5, 128, 4), (48, 64, 4), (128, 128, 8), (100, 128, 4)])
+def test_prefill_page_sizes(K, oracle, ps, d, waves):
+    """Page sizes that divide the 64-key tile (a key keeps its page slot and
+    row in every tile) and page sizes that do not (a tile spans part of a
+    page, or crosses page boundaries at varying rows), both tile widths."""
+    banner(f"prefill page size {ps}, head_dim {d}, {waves}-wave tiles")
+    q = [1, 37, 200, 64, 3, 129]
+    kv = [1, 37, 333, 700, 3, 130]
+    pool = sum((k + ps - 1) // ps for k in kv) + 9
+    w = W.make_attention(f"page_size_{ps}_{d}", q, kv, 16, 4, d, ps, pool, seed=18, device="cuda",
+                         scales="amax")
+    _check(K, oracle, w, plan=force_tile_waves(K, w, waves if d == 128 else 4))
+
+
 @pytest.mark.parametrize("hq,hk", [(32, 8), (16, 8), (8, 8), (64, 8)])
 def test_prefill_ragged_small_wide_tiles(K, oracle, hq, hk):
     """The 8-wave (256-row) head_dim-128 kernels on the small ragged batch
