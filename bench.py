@@ -153,7 +153,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": 1, "q_len": 2048, "kv_len": 2048,
                    "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128, "page_size": 16,

@@ -1,14 +1,17 @@
 // prefill.hip -- batched causal prefill attention over the NVFP4 paged KV
-// cache (gfx950, wave64, bf16 MFMA).
+// cache (gfx950, wave64, f16 MFMA).
 //
 // Design points taken from the pages, re-made for CDNA4:
 //  * FlashInfer PR #4769 page (NVFP4 KV tile repack; code analysis and "why"
 //    sections): decoding NVFP4 inside the matrix-multiply loop made the
 //    kernel instruction-bound; each KV tile is instead dequantized ONCE into a
 //    16-bit staging tile that the matrix cores then read natively.  Here: the
-//    whole workgroup decodes the tile (E2M1 x E4M3 is exact in bf16) into LDS,
-//    K and V both staged [key][d]; K feeds v_mfma_f32_32x32x16_bf16 with
-//    16-byte LDS reads, V with gfx950 LDS transpose reads.  The raw NVFP4
+//    whole workgroup decodes the tile into LDS as f16 (E2M1 x E4M3 is exact
+//    in f16, and the packed f16 multiply makes the decode one instruction
+//    per element), K and V both staged [key][d]; K feeds
+//    v_mfma_f32_32x32x16_f16 with 16-byte LDS reads, V with gfx950 LDS
+//    transpose reads.  Q enters as f16 after an exact per-row power-of-two
+//    rescale, P as f16 (11 significant bits).  The raw NVFP4
 //    bytes of the next tile are loaded into registers while the current tile
 //    is computed.  The global scales are not applied in the staging tile: g_k
 //    folds into the softmax scale and g_v into the epilogue.
@@ -36,7 +39,8 @@
 namespace nvfp4kv {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -95,9 +99,13 @@ struct Cfg {
 // against a max that may lag the true running max by up to this much.
 constexpr float kRescaleSlack = 8.0f;
 
-__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
-  // lo, hi are exactly representable in bf16: keep their upper halves.
-  return __builtin_amdgcn_perm(f2u(hi), f2u(lo), 0x07060302u);
+// Two E2M1 codes (byte SEL of x) times one E4M3 block scale, as an f16 pair:
+// the products (at most 5 significant bits, magnitudes 2^-10 .. 2688) are
+// exact in f16, so the packed f16 multiply rounds nothing.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_times(uint32_t x, f16x2 S) {
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, SEL);
+  return __builtin_bit_cast(uint32_t, c * S);
 }
 
 // Device-coherent access to the split-tile partials: raw buffer loads and
@@ -127,8 +135,7 @@ constexpr int kSchedValu = 0x2 | 0x400;  // VALU and transcendental
 constexpr int kSchedMfma = 0x8;
 constexpr int kSchedDsRead = 0x100;
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-constexpr bf16x2 kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
+constexpr f16x2 kOnesF16x2 = {(_Float16)1.0f, (_Float16)1.0f};
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -255,7 +262,7 @@ __device__ __forceinline__ void pin_jobs(RawJob<D>* job) {
   for (int j = 0; j < Cfg<D, G, W>::JOBS_PER_THREAD; ++j) asm volatile("" : "+v"(job[j].pk), "+v"(job[j].sfrow));
 }
 
-// Dequantize a job (e2m1 x E4M3 is exact in bf16) into its staged row;
+// Dequantize a job (e2m1 x E4M3 is exact in f16) into its staged row;
 // dead keys stage zeros.
 template <int D, int G, int W>
 __device__ __forceinline__ void stage_jobs(RawJob<D>* job, bool live, uint8_t* smem, int tid) {
@@ -272,14 +279,11 @@ __device__ __forceinline__ void stage_jobs(RawJob<D>* job, bool live, uint8_t* s
     const f32x2 S01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw, 1.0f, false);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {  // 8 elements per packed dword
-      const float S = w < 2 ? S01[0] : S01[1];
+      const _Float16 S = (_Float16)(w < 2 ? S01[0] : S01[1]);  // exact
+      const f16x2 SS = {S, S};
       const uint32_t x = job[j].pk[w];
-      f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 0);
-      f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 1);
-      f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 2);
-      f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 3);
-      const u32x4 o = {bf16_pair(f0[0] * S, f0[1] * S), bf16_pair(f1[0] * S, f1[1] * S),
-                       bf16_pair(f2[0] * S, f2[1] * S), bf16_pair(f3[0] * S, f3[1] * S)};
+      const u32x4 o = {fp4x2_times<0>(x, SS), fp4x2_times<1>(x, SS), fp4x2_times<2>(x, SS),
+                       fp4x2_times<3>(x, SS)};
       *(u32x4*)(rowp + (part * 4 + w) * 16) = o;
     }
   }
@@ -303,7 +307,7 @@ struct TileStager {
   using C = Cfg<D, G, W>;
   static constexpr int PIECES = 8 * C::JOBS_PER_THREAD;
   uint8_t* rowp[C::JOBS_PER_THREAD];
-  f32x2 S01[C::JOBS_PER_THREAD];
+  uint32_t S01[C::JOBS_PER_THREAD];  // the part's two E4M3 scales as an f16 pair (exact)
   u32x4 chunk;
   __device__ __forceinline__ TileStager(const RawJob<D>* job, bool live, uint8_t* smem, int tid) {
 #pragma unroll
@@ -315,18 +319,19 @@ struct TileStager {
       rowp[j] = (tensor ? smem + C::K_STAGE + key * C::VROW : smem + key * C::KROW) + part * 64;
       // both E4M3 scales of the part in one conversion (dead keys: zero scales)
       const uint32_t sw = live ? scale_word<D>(job[j], part) >> (16 * (part & 1)) : 0u;
-      S01[j] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw, 1.0f, false);
+      const f32x2 S = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw, 1.0f, false);
+      const f16x2 Sh = {(_Float16)S[0], (_Float16)S[1]};
+      S01[j] = __builtin_bit_cast(uint32_t, Sh);
     }
   }
   template <int P>
   __device__ __forceinline__ void piece(const RawJob<D>* job) {
     constexpr int j = P / 8, w = (P / 2) % 4, h = P % 2;
-    const float S = w < 2 ? S01[j][0] : S01[j][1];
+    const _Float16 S = __builtin_bit_cast(f16x2, S01[j])[w < 2 ? 0 : 1];
+    const f16x2 SS = {S, S};
     const uint32_t x = job[j].pk[w];
-    const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 2 * h);
-    const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 2 * h + 1);
-    chunk[2 * h] = bf16_pair(f0[0] * S, f0[1] * S);
-    chunk[2 * h + 1] = bf16_pair(f1[0] * S, f1[1] * S);
+    chunk[2 * h] = fp4x2_times<2 * h>(x, SS);
+    chunk[2 * h + 1] = fp4x2_times<2 * h + 1>(x, SS);
     if constexpr (h == 1) *(u32x4*)(rowp[j] + w * 16) = chunk;
   }
 };
@@ -409,17 +414,36 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   const float gk = *a.kscale, gv = *a.vscale;
   if (tile == 0 && tid == 0 && !(scale_ok(gk) && scale_ok(gv)))
     atomicOr(a.err, (uint32_t)NVFP4KV_DEV_BAD_SCALE_ATTN);
-  const float cscale = a.sm_scale_log2 * gk;  // scores -> log2 domain
-
-  // ---- Q^T operand fragments: lane holds Q[row][16c + 8hh .. +7]
-  bf16x8 qf[C::NDC];
+  // ---- Q^T operand fragments: lane holds Q[row][16c + 8hh .. +7], in f16
+  // after an exact power-of-two rescale of the row: bf16 values have 8
+  // significant bits, and the row's largest magnitude goes to [2^14, 2^15),
+  // so every value within 2^-28 of it stays a normal f16.  The row's scale
+  // comes back in its score scale.
+  f16x8 qf[C::NDC];
+  float cscale;  // scores -> log2 domain
   {
     const uint16_t* qrow = a.q + ((int64_t)(q_begin + (row_valid ? tok : q0)) * a.Hq + hq) * D;
+    u32x4 qw[C::NDC];
+    uint32_t am = 0;  // largest |bf16| bit pattern of the row
 #pragma unroll
     for (int c = 0; c < C::NDC; ++c) {
-      u32x4 w = *(const u32x4*)(qrow + c * 16 + hh * 8);
-      __builtin_memcpy(&qf[c], &w, 16);
+      qw[c] = *(const u32x4*)(qrow + c * 16 + hh * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) am = max(am, max(qw[c][e] & 0x7FFFu, (qw[c][e] >> 16) & 0x7FFFu));
     }
+    am = max(am, (uint32_t)__shfl_xor((int)am, 32));  // the row's other half
+    const int sh = am >= 0x80u ? min(max((int)(am >> 7) - 127 - 14, -100), 113) : 0;
+    const float down = u2f((uint32_t)(127 - sh) << 23);  // 2^-sh
+    cscale = a.sm_scale_log2 * gk * u2f((uint32_t)(127 + sh) << 23);
+#pragma unroll
+    for (int c = 0; c < C::NDC; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f16x2 h = {(_Float16)(u2f(qw[c][e] << 16) * down), (_Float16)(u2f(qw[c][e] & 0xFFFF0000u) * down)};
+        qw[c][e] = __builtin_bit_cast(uint32_t, h);
+      }
+#pragma unroll
+    for (int c = 0; c < C::NDC; ++c) __builtin_memcpy(&qf[c], &qw[c], 16);
     // Consume the Q fragments here, so their load waits are placed before the
     // KV loop rather than inside it (where they would also wait for the
     // prefetch of the next tile).
@@ -463,9 +487,9 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     constexpr int NQK = 2 * C::NDC, KA = 3;
     f32x16 s[2];
     s[0] = s[1] = (f32x16){};
-    bf16x8 kf[KA];
+    f16x8 kf[KA];
     auto kread = [&](int i) {
-      bf16x8 v;
+      f16x8 v;
       __builtin_memcpy(&v, sK + ((i & 1) * 32 + n) * C::KROW + hh * 16 + (i >> 1) * 32, 16);
       return v;
     };
@@ -474,7 +498,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     TileStager<D, G, W> stager(job, live, smem + ((jt + 1) & 1) * STG, tid);
     static_for<0, NQK>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % KA], qf[i >> 1], s[i & 1], 0, 0, 0);
+      s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[i % KA], qf[i >> 1], s[i & 1], 0, 0, 0);
       if constexpr (i + KA < NQK) kf[i % KA] = kread(i + KA);
       // staging pieces [P0, P1) in this slot
       constexpr int HP = TileStager<D, G, W>::PIECES;
@@ -521,7 +545,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     const float m_sub = m_new == -__builtin_inff() ? 0.0f : m_new;
 
     // ---- P^T operands straight from the accumulators, one 16-key chunk kc
-    // at a time (elements 8(kc&1)..+7 of s[kc/2]), rounded to bf16; the row
+    // at a time (elements 8(kc&1)..+7 of s[kc/2]), rounded to f16; the row
     // sum adds the rounded values (the weights the products use).
     // O^T += V^T P^T with V^T fragments by transpose reads of the [key][d]
     // stage: keys 4hh..4hh+3 and 8+4hh..8+4hh+3 of each chunk (the P^T
@@ -533,20 +557,20 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     auto exps = [&](int kc, int j) {  // pair j of chunk kc
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kc >> 1][8 * (kc & 1) + 2 * j], cscale, -m_sub));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kc >> 1][8 * (kc & 1) + 2 * j + 1], cscale, -m_sub));
-      const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnesBf16x2, l_run, false);
+      const f16x2 pp = {(_Float16)p0, (_Float16)p1};
+      l_run = __builtin_amdgcn_fdot2(pp, kOnesF16x2, l_run, false);
       pw[kc][j] = __builtin_bit_cast(uint32_t, pp);
     };
     auto vread = [&](int i) {  // MFMA i: chunk i / NDB, head_dim block i % NDB
       const uint8_t* vp = vbase + (i / C::NDB) * 16 * C::VROW + (i % C::NDB) * 64;
       const s16x4 lo = lds_read_tr16(vp);
       const s16x4 hi = lds_read_tr16(vp + 8 * C::VROW);
-      bf16x8 vf;
+      f16x8 vf;
       __builtin_memcpy(&vf, &lo, 8);
       __builtin_memcpy((char*)&vf + 8, &hi, 8);
       return vf;
     };
-    bf16x8 vf[VA];
+    f16x8 vf[VA];
 #pragma unroll
     for (int i = 0; i < VA; ++i) vf[i] = vread(i);
 #pragma unroll
@@ -555,9 +579,9 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     static_for<0, NPV>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       constexpr int kc = i / C::NDB, db = i % C::NDB;
-      bf16x8 pf;
+      f16x8 pf;
       __builtin_memcpy(&pf, pw[kc], 16);
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % VA], pf, o[db], 0, 0, 0);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[i % VA], pf, o[db], 0, 0, 0);
       if constexpr (i + VA < NPV) vf[i % VA] = vread(i + VA);
       if constexpr (kc + 1 < 4) {
         // pairs [J0, J1) of chunk kc+1 in this slot
