@@ -1,5 +1,5 @@
 // decode.hip -- one decode step of attention over the NVFP4 paged cache
-// (gfx950, wave64, bf16 MFMA).
+// (gfx950, wave64, f16 MFMA).
 //
 // The step that follows the prefill in serving, on the same cache, codecs and
 // page table: every request has one new query token, already appended, that
@@ -12,7 +12,7 @@
 // workgroup with the KV head fastest: the waves of a workgroup read the
 // different heads' slices of the same token rows together, so each cache line
 // comes from HBM once and serves them all from the CU's caches.  64-key tiles:
-//  * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 contraction
+//  * S^T = K Q^T with v_mfma_f32_16x16x32_f16: A = 16 keys x 32 contraction
 //    elements, B = Q^T with the G query heads of the KV head as its columns
 //    (columns >= G are zero).  The head_dim contraction runs in a lane-shaped
 //    order: lane (key k, quarter q) supplies, in MFMA c, head_dim elements
@@ -21,11 +21,13 @@
 //    registers.  K needs no LDS: each K element feeds one wave only.
 //  * Online softmax per query head in the log2 domain with the prefill's lazy
 //    rescaling; the four lanes of a head (one per quarter) share its max.
-//  * O^T += V^T P^T with v_mfma_f32_16x16x32_bf16: V is dequantized into the
+//  * O^T += V^T P^T with v_mfma_f32_16x16x32_f16: V is dequantized into the
 //    wave's own LDS rows [key][d] and read back with transpose reads in the
 //    key order in which the S^T accumulators hold P^T.
-// E2M1 x E4M3 is exact in bf16; g_k folds into the softmax scale and g_v
-// into the output.
+// E2M1 x E4M3 is exact in f16 (and one packed f16 multiply applies a block
+// scale to two elements); the bf16 queries enter as f16 after an exact
+// per-head power-of-two rescale, P as f16.  g_k folds into the softmax scale
+// and g_v into the output.
 #include <hip/hip_runtime.h>
 
 #include "nvfp4kv_codec.hpp"
@@ -34,7 +36,8 @@
 namespace nvfp4kv {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -42,7 +45,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
+constexpr f16x2 kOnes = {(_Float16)1.0f, (_Float16)1.0f};
 constexpr float kRescaleSlack = 8.0f;  // log2 units, as in the prefill
 constexpr int kWaves = 8;              // independent waves per workgroup
 
@@ -51,7 +54,7 @@ struct DCfg {
   static constexpr int NQ = D / 4;         // head_dim elements per lane quarter
   static constexpr int NC = NQ / 8;        // QK MFMAs per 16-key block (8 elements each)
   static constexpr int NDB = D / 16;       // 16-row head_dim blocks of O^T
-  static constexpr int VROW = 2 * D + 32;  // padded bf16 V row in LDS (bytes)
+  static constexpr int VROW = 2 * D + 32;  // padded f16 V row in LDS (bytes)
   static constexpr int LDS_WAVE = 64 * VROW;
 };
 
@@ -77,10 +80,6 @@ struct DecodeArgs {
   float sm_scale_log2;
 };
 
-__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
-  // lo, hi are exactly representable in bf16: keep their upper halves.
-  return __builtin_amdgcn_perm(f2u(hi), f2u(lo), 0x07060302u);
-}
 
 // One lane's quarter rows of a 64-key tile: for each 16-key block kb, the
 // NQ/2 code bytes of K and of V and their scale bytes (two blocks of 16 for
@@ -91,15 +90,19 @@ struct Raw {
   uint32_t ksf[4], vsf[4];
 };
 
-// 8 codes (one dword) times the E4M3 scale S, as 8 bf16 values.
-__device__ __forceinline__ bf16x8 dequant8(uint32_t x, float S) {
-  const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 0);
-  const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 1);
-  const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 2);
-  const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, 3);
-  const u32x4 w = {bf16_pair(f0[0] * S, f0[1] * S), bf16_pair(f1[0] * S, f1[1] * S),
-                   bf16_pair(f2[0] * S, f2[1] * S), bf16_pair(f3[0] * S, f3[1] * S)};
-  return __builtin_bit_cast(bf16x8, w);
+// 8 codes (one dword) times the E4M3 scale S, as 8 f16 values: two codes
+// per conversion, one packed multiply per pair (the products have at most 5
+// significant bits and lie in 2^-10 .. 2688: exact in f16).
+__device__ __forceinline__ f16x8 dequant8(uint32_t x, float S) {
+  const _Float16 s = (_Float16)S;  // exact (an E4M3 value)
+  const f16x2 ss = {s, s};
+  const f16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 0) * ss;
+  const f16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 1) * ss;
+  const f16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 2) * ss;
+  const f16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 3) * ss;
+  const u32x4 w = {__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
+                   __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)};
+  return __builtin_bit_cast(f16x8, w);
 }
 
 template <int D, int G>
@@ -127,17 +130,35 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   const float gk = *a.kscale, gv = *a.vscale;
   if (item == 0 && lane == 0 && !(scale_ok(gk) && scale_ok(gv)))
     atomicOr(a.err, (uint32_t)NVFP4KV_DEV_BAD_SCALE_ATTN);
-  const float cscale = a.sm_scale_log2 * gk;
-
-  // ---- Q^T operand: lane (row, qq) holds Q[row][qq*NQ + 8c .. +7] for MFMA c
-  bf16x8 qf[C::NC];
+  // ---- Q^T operand: lane (row, qq) holds Q[row][qq*NQ + 8c .. +7] for MFMA c,
+  // in f16 after an exact power-of-two rescale of the query head's row (its
+  // largest magnitude to [2^14, 2^15)), folded back into its score scale
+  f16x8 qf[C::NC];
+  float cscale;
   {
     const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + hk * G + min(row, G - 1)) * D + qq * C::NQ;
+    u32x4 qw[C::NC];
+    uint32_t am = 0;  // largest |bf16| bit pattern of the row
 #pragma unroll
     for (int c = 0; c < C::NC; ++c) {
-      u32x4 w = *(const u32x4*)(qrow + 8 * c);
-      if (row >= G) w = (u32x4){0u, 0u, 0u, 0u};
-      qf[c] = __builtin_bit_cast(bf16x8, w);
+      qw[c] = *(const u32x4*)(qrow + 8 * c);
+      if (row >= G) qw[c] = (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) am = max(am, max(qw[c][e] & 0x7FFFu, (qw[c][e] >> 16) & 0x7FFFu));
+    }
+    am = max(am, (uint32_t)__shfl_xor((int)am, 16));  // the row's other quarters
+    am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+    const int sh = am >= 0x80u ? min(max((int)(am >> 7) - 127 - 14, -100), 113) : 0;
+    const float down = u2f((uint32_t)(127 - sh) << 23);  // 2^-sh
+    cscale = a.sm_scale_log2 * gk * u2f((uint32_t)(127 + sh) << 23);
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f16x2 h = {(_Float16)(u2f(qw[c][e] << 16) * down), (_Float16)(u2f(qw[c][e] & 0xFFFF0000u) * down)};
+        qw[c][e] = __builtin_bit_cast(uint32_t, h);
+      }
+      qf[c] = __builtin_bit_cast(f16x8, qw[c]);
     }
   }
 
@@ -217,8 +238,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
       s[kb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < C::NC; ++c) {
-        const bf16x8 kf = dequant8(raw.k[kb][c], c < C::NC / 2 ? S[0] : S[1]);
-        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c], s[kb], 0, 0, 0);
+        const f16x8 kf = dequant8(raw.k[kb][c], c < C::NC / 2 ? S[0] : S[1]);
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[c], s[kb], 0, 0, 0);
       }
     }
     // ---- stage V (this lane's quarter rows) into the wave's LDS rows
@@ -228,7 +249,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
       uint8_t* vrow = vst + (16 * kb + k16) * C::VROW + qq * C::NQ * 2;
 #pragma unroll
       for (int c = 0; c < C::NC; ++c)
-        *(bf16x8*)(vrow + 16 * c) = dequant8(raw.v[kb][c], c < C::NC / 2 ? S[0] : S[1]);
+        *(f16x8*)(vrow + 16 * c) = dequant8(raw.v[kb][c], c < C::NC / 2 ? S[0] : S[1]);
     }
     // ---- keys past the request's end (last tile only)
     const int kbase = k0 + 64 * t;
@@ -258,9 +279,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
       for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
     }
     // P^T for the 32 keys of half m: keys 32m + 4qq + r (block 2m), then
-    // 32m + 16 + 4qq + r (block 2m+1); rounded to bf16, the row sum adds the
+    // 32m + 16 + 4qq + r (block 2m+1); rounded to f16, the row sum adds the
     // rounded values
-    bf16x8 pf[2];
+    f16x8 pf[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       uint32_t pw[4];
@@ -270,8 +291,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
         for (int r2 = 0; r2 < 2; ++r2) {
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m + h][2 * r2], cscale, -m_new));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m + h][2 * r2 + 1], cscale, -m_new));
-          const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes, l_run, false);
+          const f16x2 pp = {(_Float16)p0, (_Float16)p1};
+          l_run = __builtin_amdgcn_fdot2(pp, kOnes, l_run, false);
           pw[2 * h + r2] = __builtin_bit_cast(uint32_t, pp);
         }
       __builtin_memcpy(&pf[m], pw, 16);
@@ -284,10 +305,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
         const uint8_t* vp = vst + voff + 32 * m * C::VROW + 16 * db * 2;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 16 * C::VROW));
-        bf16x8 vf;
+        f16x8 vf;
         __builtin_memcpy(&vf, &lo, 8);
         __builtin_memcpy((char*)&vf + 8, &hi, 8);
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[m], o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[m], o[db], 0, 0, 0);
       }
     raw = nraw;
 #pragma unroll
