@@ -67,6 +67,10 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--no-achievable", action="store_true",
                     help="skip the measured achievable peaks (copy, MFMA-only loop)")
+    ap.add_argument("--no-ablation", action="store_true",
+                    help="skip the dequant-placement ablation of the prefill")
+    ap.add_argument("--ablation-only", action="store_true",
+                    help="only launch the prefill under the three dequant placements (for counters)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (HBM-counter calibration)")
     args = ap.parse_args()
@@ -103,6 +107,11 @@ def main():
     kvp_d, pt_d = kvp_h.to(dev), torch.from_numpy(w.page_table).to(dev)
     out = torch.empty_like(w.q)
 
+    if args.ablation_only:
+        cache.append(w.k, w.v, w.slot_mapping)
+        print(json.dumps({"dequant_ablation": bench_dequant_ablation(
+            K, w, cache, (qo_d, kvp_d, pt_d, kvl_d), out, torch, per_graph=10, replays=2)}), flush=True)
+        return
     t0 = time.perf_counter()
     nplan = 200
     for _ in range(nplan):
@@ -176,6 +185,9 @@ def main():
         result["append_stress"] = bench_append_stress(K, W, dev, torch, np)
     if not args.no_decode:
         result["decode"] = bench_decode(K, W, dev, torch, np)
+    if not args.no_ablation:
+        result["dequant_ablation"] = bench_dequant_ablation(K, w, cache, (qo_d, kvp_d, pt_d, kvl_d), out,
+                                                            torch)
     if not args.no_achievable:
         ach = bench_achievable(dev, torch, np)
         ach["prefill_frac_of_mfma_loop"] = round(pre_tflops / ach["mfma_bf16_TFLOPs"], 4)
@@ -210,6 +222,25 @@ def graph_launch_ms(torch, fn, per_graph=50, replays=20):
     torch.cuda.synchronize()
     del graph
     return e0.elapsed_time(e1) / (per_graph * replays)
+
+
+def bench_dequant_ablation(K, w, cache, dev_args, out, torch, per_graph=50, replays=20):
+    """The 2048x2048 prefill under the three dequant placements of the PR #4769
+    page's comparison (graph-timed launches; 4-wave tiles, as the plan picks):
+    tiles decoded once per workgroup into f16 LDS (the kernel's own design), K
+    decoded in registers inside the matrix loop, and a byte-table decode."""
+    flops = attention_flops(w.q_lens, w.kv_lens, w.num_q_heads, w.head_dim)
+    res = {}
+    for mode, name in ((0, "lds_once_per_tile"), (1, "k_in_loop_registers"), (2, "lds_byte_table")):
+        plan = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), w.num_q_heads,
+                      w.num_kv_heads, w.head_dim, w.page_size, kv_indptr=torch.from_numpy(w.kv_indptr),
+                      tile_waves=4, dequant_mode=mode)
+        ms = graph_launch_ms(torch, lambda: K.paged_prefill_causal(w.q, *dev_args, cache, out, w.sm_scale,
+                                                                   plan=plan), per_graph, replays)
+        res[name] = {"dequant_mode": mode, "avg_launch_us": round(ms * 1e3, 2),
+                     "TFLOP_s": round(flops / (ms * 1e-3) / 1e12, 1),
+                     "frac": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    return res
 
 
 def bench_plan(K, torch, np, batches=(64, 256, 1024), reps=50):

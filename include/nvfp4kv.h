@@ -132,6 +132,18 @@ typedef struct {
   int32_t max_chunks;       /* chunks of the most split Q tile */
   int64_t num_items;        /* workgroups launched: Q tiles, or their KV chunks */
   int64_t num_split_tiles;  /* Q tiles (x KV heads) whose KV range is split */
+  /* Dequant-placement ablation (the PR #4769 page's before/after comparison);
+     the plan sets 0 and a caller may change it before paged_prefill_causal:
+       0  each NVFP4 KV tile decoded once per workgroup into an f16 LDS tile
+          (hardware FP4 conversion) -- the kernel's own design;
+       1  K codes and scales staged raw in LDS, every wave decoding its K
+          operand fragments in registers inside the matrix loop (V as 0);
+       2  as 0, decoding the codes with a byte table (v_perm) instead of the
+          hardware conversion.
+     1 and 2 exist for head_dim 128, GQA group 4, 4-wave tiles (block_q 32)
+     and page sizes dividing 64; other shapes return NVFP4KV_EUNSUPPORTED.
+     All three give results within the same tolerance of the oracle. */
+  int32_t dequant_mode;
 } nvfp4kv_prefill_plan;
 
 /*

@@ -60,7 +60,8 @@ class PlanStruct(ctypes.Structure):
                [(n, ctypes.c_int64) for n in
                 ("num_tiles", "kv_bytes", "l2_bytes", "workspace_bytes")] + \
                [("split_len", ctypes.c_int32), ("max_chunks", ctypes.c_int32),
-                ("num_items", ctypes.c_int64), ("num_split_tiles", ctypes.c_int64)]
+                ("num_items", ctypes.c_int64), ("num_split_tiles", ctypes.c_int64),
+                ("dequant_mode", ctypes.c_int32)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -267,7 +268,8 @@ class Plan:
     max lengths from tensor reductions, lengths cast to int32 at entry)."""
 
     def __init__(self, qo_indptr, kv_lens, num_q_heads, num_kv_heads, head_dim, page_size,
-                 kv_indptr=None, l2_bytes: int = 0, split_len: int = 0, tile_waves: int = 0):
+                 kv_indptr=None, l2_bytes: int = 0, split_len: int = 0, tile_waves: int = 0,
+                 dequant_mode: int = 0):
         qo = _host_int32(qo_indptr, "qo_indptr")
         kvl = _host_int32(kv_lens, "kv_lens")
         kvp = _host_int32(kv_indptr, "kv_indptr") if kv_indptr is not None else None
@@ -278,6 +280,7 @@ class Plan:
             _ptr(qo), _ptr(kvl), _ptr(kvp), kvl.numel(), num_q_heads, num_kv_heads, head_dim,
             page_size, l2_bytes, split_len, tile_waves, ctypes.byref(self.struct)),
             "nvfp4_prefill_plan")
+        self.struct.dequant_mode = int(dequant_mode)
         self.qo_host, self.kv_lens_host = qo, kvl
         self._workspace = {}
 
@@ -309,12 +312,14 @@ def _host_int32(t, name) -> torch.Tensor:
 
 
 def plan(qo_indptr, kv_lens, num_q_heads, num_kv_heads, head_dim, page_size, kv_indptr=None,
-         l2_bytes: int = 0, split_len: int = 0, tile_waves: int = 0) -> Plan:
+         l2_bytes: int = 0, split_len: int = 0, tile_waves: int = 0, dequant_mode: int = 0) -> Plan:
     """Host plan of one prefill batch.  split_len: KV tiles per chunk of a split
     Q tile (0 automatic, > 0 forced, < 0 never); tile_waves: waves of 32 query
-    rows per workgroup (0 automatic, 4 or 8)."""
+    rows per workgroup (0 automatic, 4 or 8); dequant_mode: the dequant-placement
+    ablation (0: tiles decoded once into f16 LDS, the default; 1: K decoded in
+    registers inside the matrix loop; 2: byte-table decode)."""
     return Plan(qo_indptr, kv_lens, num_q_heads, num_kv_heads, head_dim, page_size, kv_indptr,
-                l2_bytes, split_len, tile_waves)
+                l2_bytes, split_len, tile_waves, dequant_mode)
 
 
 def paged_prefill_causal(q: torch.Tensor, qo_indptr: torch.Tensor, kv_indptr: torch.Tensor,

@@ -235,4 +235,4 @@ extern "C" const char* nvfp4kv_status_string(int status) {
   }
 }
 
-extern "C" int nvfp4kv_abi_version(void) { return 100; }
+extern "C" int nvfp4kv_abi_version(void) { return 101; }

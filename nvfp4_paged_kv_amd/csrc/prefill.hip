@@ -85,6 +85,9 @@ struct Cfg {
   static constexpr int KROW = D * 2 + 16;
   static constexpr int VROW = D * 2 + 32;
   static constexpr int K_STAGE = BN * KROW;
+  // Raw K row of the in-loop decode ablation: 64 code bytes + 8 scale bytes
+  // (4-byte code reads of 32 keys x 2 halves hit 64 distinct banks)
+  static constexpr int KRAW = 72;
   static constexpr int V_STAGE = BN * VROW;
   static constexpr int NDC = D / 16;        // MFMA k-steps over head_dim
   static constexpr int NDB = D / 32;        // 32-wide head_dim blocks of O^T
@@ -130,12 +133,50 @@ __device__ __forceinline__ float coherent_load1(__amdgpu_buffer_rsrc_t r, int of
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kDeviceScopePolicy));
 }
 
+// max(x, x of lane l ^ 32) in every lane: one v_permlane32_swap exchanges
+// the wave's halves in registers (no LDS round trip).
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+  return __builtin_fmaxf(u2f(r[0]), u2f(r[1]));
+}
+
 // Instruction classes of the scheduling-group hints.
 constexpr int kSchedValu = 0x2 | 0x400;  // VALU and transcendental
 constexpr int kSchedMfma = 0x8;
 constexpr int kSchedDsRead = 0x100;
 
 constexpr f16x2 kOnesF16x2 = {(_Float16)1.0f, (_Float16)1.0f};
+
+// Dequantization kinds (the dequant-placement ablation; 0 is the kernel's own):
+//  0: each KV tile decoded once per workgroup into the f16 staging tile, with
+//     the hardware FP4 conversion;
+//  1: K codes and scales staged raw, each wave decoding its K fragments in
+//     registers inside the matrix loop (the page's "before" design); V as 0;
+//  2: as 0, with a byte-table decode of the codes instead of the hardware
+//     conversion.
+// Eight codes (one dword) times the f16 scale pair SS, as four f16 pairs.
+template <int DQ>
+__device__ __forceinline__ u32x4 decode8(uint32_t x, f16x2 SS) {
+  if constexpr (DQ != 2) {
+    return (u32x4){fp4x2_times<0>(x, SS), fp4x2_times<1>(x, SS), fp4x2_times<2>(x, SS),
+                   fp4x2_times<3>(x, SS)};
+  } else {
+    // high bytes of the f16 of the E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6
+    // (their low bytes are 0): byte k of (kLutHi:kLutLo), chosen by v_perm
+    constexpr uint32_t kLutLo = 0x3E3C3800u, kLutHi = 0x46444240u;
+    const uint32_t ev = x & 0x07070707u, od = (x >> 4) & 0x07070707u;  // even / odd element codes
+    const uint32_t hev = __builtin_amdgcn_perm(kLutHi, kLutLo, ev) | ((x & 0x08080808u) << 4);
+    const uint32_t hod = __builtin_amdgcn_perm(kLutHi, kLutLo, od) | (x & 0x80808080u);
+    u32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // element pair j: f16 (hev byte j) << 8 and (hod byte j) << 8
+      const uint32_t pair = __builtin_amdgcn_perm(hod, hev, 0x000C000Cu | (uint32_t)j << 8 | (uint32_t)(4 + j) << 24);
+      r[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, pair) * SS);
+    }
+    return r;
+  }
+}
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -262,33 +303,6 @@ __device__ __forceinline__ void pin_jobs(RawJob<D>* job) {
   for (int j = 0; j < Cfg<D, G, W>::JOBS_PER_THREAD; ++j) asm volatile("" : "+v"(job[j].pk), "+v"(job[j].sfrow));
 }
 
-// Dequantize a job (e2m1 x E4M3 is exact in f16) into its staged row;
-// dead keys stage zeros.
-template <int D, int G, int W>
-__device__ __forceinline__ void stage_jobs(RawJob<D>* job, bool live, uint8_t* smem, int tid) {
-  using C = Cfg<D, G, W>;
-#pragma unroll
-  for (int j = 0; j < C::JOBS_PER_THREAD; ++j) {
-    const int id = tid + C::NT * j;
-    const int tensor = id / (C::BN * C::PARTS);
-    const int rem = id - tensor * C::BN * C::PARTS;
-    const int key = rem / C::PARTS, part = rem % C::PARTS;
-    uint8_t* rowp = tensor ? smem + C::K_STAGE + key * C::VROW : smem + key * C::KROW;
-    // both E4M3 scales of the part in one conversion (dead keys: zero scales)
-    const uint32_t sw = live ? scale_word<D>(job[j], part) >> (16 * (part & 1)) : 0u;
-    const f32x2 S01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw, 1.0f, false);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {  // 8 elements per packed dword
-      const _Float16 S = (_Float16)(w < 2 ? S01[0] : S01[1]);  // exact
-      const f16x2 SS = {S, S};
-      const uint32_t x = job[j].pk[w];
-      const u32x4 o = {fp4x2_times<0>(x, SS), fp4x2_times<1>(x, SS), fp4x2_times<2>(x, SS),
-                       fp4x2_times<3>(x, SS)};
-      *(u32x4*)(rowp + (part * 4 + w) * 16) = o;
-    }
-  }
-}
-
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
 template <int B, int E, class F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -302,12 +316,14 @@ __device__ __forceinline__ void static_for(F&& f) {
 // dequantizes 8 elements (word (p/2)%4 of job p/8, its low or high half) and
 // every second piece stores the finished 16-byte chunk.  The pieces are
 // interleaved with the matrix instructions of the tile before.
-template <int D, int G, int W>
+template <int D, int G, int W, int DQ = 0>
 struct TileStager {
   using C = Cfg<D, G, W>;
   static constexpr int PIECES = 8 * C::JOBS_PER_THREAD;
   uint8_t* rowp[C::JOBS_PER_THREAD];
   uint32_t S01[C::JOBS_PER_THREAD];  // the part's two E4M3 scales as an f16 pair (exact)
+  uint32_t sw[C::JOBS_PER_THREAD];   // the part's two raw scale bytes
+  uint8_t* sfp;                      // (DQ 1) where the K part's scale bytes go
   u32x4 chunk;
   __device__ __forceinline__ TileStager(const RawJob<D>* job, bool live, uint8_t* smem, int tid) {
 #pragma unroll
@@ -316,10 +332,12 @@ struct TileStager {
       const int tensor = id / (C::BN * C::PARTS);
       const int rem = id - tensor * C::BN * C::PARTS;
       const int key = rem / C::PARTS, part = rem % C::PARTS;
-      rowp[j] = (tensor ? smem + C::K_STAGE + key * C::VROW : smem + key * C::KROW) + part * 64;
+      rowp[j] = tensor ? smem + C::K_STAGE + key * C::VROW + part * 64
+                       : (DQ == 1 ? smem + key * C::KRAW + part * 16 : smem + key * C::KROW + part * 64);
+      if (j == 0) sfp = smem + key * C::KRAW + 64 + 2 * part;
       // both E4M3 scales of the part in one conversion (dead keys: zero scales)
-      const uint32_t sw = live ? scale_word<D>(job[j], part) >> (16 * (part & 1)) : 0u;
-      const f32x2 S = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw, 1.0f, false);
+      sw[j] = live ? (scale_word<D>(job[j], part) >> (16 * (part & 1))) & 0xFFFFu : 0u;
+      const f32x2 S = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw[j], 1.0f, false);
       const f16x2 Sh = {(_Float16)S[0], (_Float16)S[1]};
       S01[j] = __builtin_bit_cast(uint32_t, Sh);
     }
@@ -327,16 +345,30 @@ struct TileStager {
   template <int P>
   __device__ __forceinline__ void piece(const RawJob<D>* job) {
     constexpr int j = P / 8, w = (P / 2) % 4, h = P % 2;
-    const _Float16 S = __builtin_bit_cast(f16x2, S01[j])[w < 2 ? 0 : 1];
-    const f16x2 SS = {S, S};
-    const uint32_t x = job[j].pk[w];
-    chunk[2 * h] = fp4x2_times<2 * h>(x, SS);
-    chunk[2 * h + 1] = fp4x2_times<2 * h + 1>(x, SS);
-    if constexpr (h == 1) *(u32x4*)(rowp[j] + w * 16) = chunk;
+    if constexpr (DQ == 1 && j == 0) {
+      // raw K: the part's 16 code bytes and its 2 scale bytes (job 0 is K
+      // for 4-wave tiles, the only ones the ablation is built for)
+      static_assert(C::JOBS_PER_THREAD == 2, "in-loop decode ablation: 4-wave tiles");
+      if constexpr (P == 7) {
+        *(u32x4*)rowp[0] = job[0].pk;
+        *(uint16_t*)sfp = (uint16_t)sw[0];
+      }
+    } else {
+      const _Float16 S = __builtin_bit_cast(f16x2, S01[j])[w < 2 ? 0 : 1];
+      const f16x2 SS = {S, S};
+      const uint32_t x = job[j].pk[w];
+      if constexpr (DQ == 2) {
+        if constexpr (h == 1) *(u32x4*)(rowp[j] + w * 16) = decode8<2>(x, SS);
+      } else {
+        chunk[2 * h] = fp4x2_times<2 * h>(x, SS);
+        chunk[2 * h + 1] = fp4x2_times<2 * h + 1>(x, SS);
+        if constexpr (h == 1) *(u32x4*)(rowp[j] + w * 16) = chunk;
+      }
+    }
   }
 };
 
-template <int D, int G, int W, bool PA>
+template <int D, int G, int W, bool PA, int DQ>
 __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   using C = Cfg<D, G, W>;
   // Two staging buffers: tile j+1 is dequantized into one while tile j is
@@ -464,7 +496,10 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   // Pipeline prologue: the first tile staged (into buffer jt_begin & 1), the
   // next tile's NVFP4 bytes and the one after's page ids in flight.
   pin_jobs<D, G, W>(job);
-  stage_jobs<D, G, W>(job, live, smem + (jt_begin & 1) * STG, tid);
+  {
+    TileStager<D, G, W, DQ> st(job, live, smem + (jt_begin & 1) * STG, tid);
+    static_for<0, TileStager<D, G, W, DQ>::PIECES>([&](auto pc) { st.template piece<decltype(pc)::value>(job); });
+  }
   live = ka.load(a, job, jt_begin + 1, page_next, page_bad);
   page_next = ka.lookup(a, jt_begin + 2);
   __syncthreads();
@@ -489,19 +524,30 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     s[0] = s[1] = (f32x16){};
     f16x8 kf[KA];
     auto kread = [&](int i) {
-      f16x8 v;
-      __builtin_memcpy(&v, sK + ((i & 1) * 32 + n) * C::KROW + hh * 16 + (i >> 1) * 32, 16);
-      return v;
+      if constexpr (DQ == 1) {
+        // decode in registers: 4 code bytes (this lane's 8 elements) and the
+        // block's scale byte of the raw K row
+        const uint8_t* row = sK + ((i & 1) * 32 + n) * C::KRAW;
+        const uint32_t x = *(const uint32_t*)(row + (i >> 1) * 8 + hh * 4);
+        const uint32_t sb = row[64 + (i >> 1)];
+        const _Float16 S = (_Float16)__builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sb, 1.0f, false)[0];
+        const f16x2 SS = {S, S};
+        return __builtin_bit_cast(f16x8, decode8<1>(x, SS));
+      } else {
+        f16x8 v;
+        __builtin_memcpy(&v, sK + ((i & 1) * 32 + n) * C::KROW + hh * 16 + (i >> 1) * 32, 16);
+        return v;
+      }
     };
 #pragma unroll
     for (int i = 0; i < KA; ++i) kf[i] = kread(i);
-    TileStager<D, G, W> stager(job, live, smem + ((jt + 1) & 1) * STG, tid);
+    TileStager<D, G, W, DQ> stager(job, live, smem + ((jt + 1) & 1) * STG, tid);
     static_for<0, NQK>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[i % KA], qf[i >> 1], s[i & 1], 0, 0, 0);
       if constexpr (i + KA < NQK) kf[i % KA] = kread(i + KA);
       // staging pieces [P0, P1) in this slot
-      constexpr int HP = TileStager<D, G, W>::PIECES;
+      constexpr int HP = TileStager<D, G, W, DQ>::PIECES;
       constexpr int P0 = (i * HP + NQK - 1) / NQK, P1 = ((i + 1) * HP + NQK - 1) / NQK;
       static_for<P0, P1>([&](auto pc) { stager.template piece<decltype(pc)::value>(job); });
       if constexpr (i == NQK - 1) {
@@ -527,7 +573,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, s[kb][i]);
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+    mx = half_max(mx);
     // Lazy rescaling: the reference max moves only when the tile's max
     // exceeds it by more than kRescaleSlack (log2 units), so p stays below
     // 2^kRescaleSlack and the O^T rescale is skipped on most tiles.
@@ -792,9 +838,9 @@ __global__ __launch_bounds__(1024) void worklist_kernel(const int32_t* __restric
 template <int D, int G, int W>
 void launch_prefill(const PrefillArgs& a, hipStream_t s) {
   if (kBlockN % a.ps_div.d == 0)
-    hipLaunchKernelGGL((prefill_kernel<D, G, W, true>), dim3(a.num_items), dim3(64 * W), 0, s, a);
+    hipLaunchKernelGGL((prefill_kernel<D, G, W, true, 0>), dim3(a.num_items), dim3(64 * W), 0, s, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, G, W, false>), dim3(a.num_items), dim3(64 * W), 0, s, a);
+    hipLaunchKernelGGL((prefill_kernel<D, G, W, false, 0>), dim3(a.num_items), dim3(64 * W), 0, s, a);
 }
 
 }  // namespace
@@ -868,6 +914,18 @@ extern "C" int paged_prefill_causal(const void* q, const int32_t* qo_indptr,
   const int G = p.num_q_heads / p.num_kv_heads;
   const int D = p.head_dim;
   const int W = p.block_q * G / 32;  // waves per tile chosen by the plan
+  if (p.dequant_mode != 0) {
+    // dequant-placement ablation: head_dim 128, GQA group 4, 4-wave tiles,
+    // page sizes dividing the KV tile
+    if (D != 128 || G != 4 || W != 4 || kBlockN % c.page_size != 0 ||
+        (p.dequant_mode != 1 && p.dequant_mode != 2))
+      return NVFP4KV_EUNSUPPORTED;
+    if (p.dequant_mode == 1)
+      hipLaunchKernelGGL((prefill_kernel<128, 4, 4, true, 1>), dim3(a.num_items), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<128, 4, 4, true, 2>), dim3(a.num_items), dim3(256), 0, s, a);
+    return hipGetLastError() == hipSuccess ? NVFP4KV_OK : NVFP4KV_EHIP;
+  }
 #define NVFP4KV_CASE(DD, GG, WW) \
   if (D == DD && G == GG && W == WW) launch_prefill<DD, GG, WW>(a, s); else
   NVFP4KV_CASE(128, 1, 4) NVFP4KV_CASE(128, 2, 4) NVFP4KV_CASE(128, 4, 4) NVFP4KV_CASE(128, 8, 4)

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol(K):
     L = ctypes.CDLL(K.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert K.lib().nvfp4kv_abi_version() == 100
+    assert K.lib().nvfp4kv_abi_version() == 101
     assert K.lib().nvfp4kv_status_string(-3).startswith(b"inconsistent")
 
 

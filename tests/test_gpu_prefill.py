@@ -191,3 +191,35 @@ def test_prefill_does_not_synchronize(K):
     K.paged_prefill_causal(w.q, *args[:3], args[3], cache, out, w.sm_scale, plan=plan)
     assert not torch.cuda.current_stream().query()
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_prefill_dequant_ablation_modes(K, oracle, mode):
+    """The dequant-placement ablation kernels (K decoded in registers inside
+    the matrix loop; byte-table decode) stage the same f16 values, so their
+    outputs equal the default kernel's bit for bit; and the oracle parity."""
+    banner(f"prefill dequant ablation mode {mode}")
+    q = [1, 37, 200, 64, 3, 129]
+    kv = [1, 37, 333, 700, 3, 130]
+    w = W.make_attention(f"dequant_mode_{mode}", q, kv, 32, 8, 128, 16, 120, seed=19, device="cuda",
+                         scales="amax")
+    base, cache, _ = run_gpu(K, w, plan=force_tile_waves(K, w, 4))
+    plan = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), 32, 8, 128, 16,
+                  kv_indptr=torch.from_numpy(w.kv_indptr), split_len=-1, tile_waves=4,
+                  dequant_mode=mode)
+    out, _, _ = run_gpu(K, w, cache=cache, plan=plan)
+    torch.cuda.synchronize()
+    assert K.read_device_error("cuda") == 0
+    assert torch.equal(out.view(torch.int16), base.view(torch.int16))
+    ref, rows = oracle_outputs(oracle, w)
+    assert_close(out.index_select(0, torch.from_numpy(rows).cuda()), ref, w.name)
+
+
+def test_prefill_dequant_ablation_unsupported_shape(K):
+    """The ablation kernels exist for head_dim 128, GQA group 4, 4-wave tiles
+    only: other shapes are refused before any launch."""
+    w = W.make_attention("dequant_mode_d64", [64], [64], 8, 2, 64, 16, 8, seed=20, device="cuda")
+    plan = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), 8, 2, 64, 16,
+                  dequant_mode=1)
+    with pytest.raises(K.NVFP4KVError, match="unsupported"):
+        run_gpu(K, w, plan=plan)
