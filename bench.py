@@ -149,7 +149,7 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     pre_tflops = flops / (pre_ms * 1e-3) / 1e12
     G = w.num_q_heads // w.num_kv_heads
-    kernel_name = f"prefill_kernel<{w.head_dim},{G},{plan.block_q * G // 32},{'true' if 64 % w.page_size == 0 else 'false'}>"
+    kernel_name = f"prefill_kernel<{w.head_dim},{G},{plan.block_q * G // 32},{'true' if 64 % w.page_size == 0 else 'false'},0>"
     traffic = _traffic("prefill_2k")
     result = {
         "metric": METRIC,
