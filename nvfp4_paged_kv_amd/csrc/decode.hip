@@ -191,8 +191,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
           r.k[kb][c] = kw[c];
           r.v[kb][c] = vw[c];
         }
-        r.ksf[kb] = *(const uint16_t*)(a.ksf + so);
-        r.vsf[kb] = *(const uint16_t*)(a.vsf + so);
+        // the key's whole 8-byte scale row (one aligned load), this lane's
+        // quarter picked from it below
+        const uint2 ks = *(const uint2*)(a.ksf + rowi * (D / 16)), vs = *(const uint2*)(a.vsf + rowi * (D / 16));
+        r.ksf[kb] = qq < 2 ? ks.x : ks.y;
+        r.vsf[kb] = qq < 2 ? vs.x : vs.y;
       } else {
         const uint2 kw = *(const uint2*)(a.kc + co), vw = *(const uint2*)(a.vc + co);
         r.k[kb][0] = kw.x;
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   };
   // the two E4M3 scales of a quarter (head_dim 64: one, used for both halves)
   auto scales = [&](uint32_t sfw) {
-    const f32x2 s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sfw, 1.0f, false);
+    const f32x2 s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(C::NC == 4 ? sfw >> (16 * (qq & 1)) : sfw, 1.0f, false);
     return C::NC == 4 ? s : (f32x2){s[0], s[0]};
   };
 
