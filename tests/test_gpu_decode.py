@@ -126,3 +126,18 @@ def test_decode_does_not_synchronize(K):
     K.paged_decode(w.q, *args, cache, out, w.sm_scale, plan)
     assert not torch.cuda.current_stream().query()
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("ps,d,chunk_len", [(1, 128, 128), (8, 64, 0), (64, 128, 64), (5, 128, 128),
+                                            (48, 64, 0), (128, 128, 192)])
+def test_decode_page_sizes(K, oracle, ps, d, chunk_len):
+    """Page sizes that divide the 64-key tile (a lane's key keeps its page
+    slot in every tile) and page sizes that do not, with one or more chunks
+    per request and lengths that end inside a tile and a page."""
+    banner(f"decode page size {ps}, head_dim {d}, chunk_len {chunk_len}")
+    kv = [1, 17, 63, 64, 65, 300, 1000, 700]
+    pool = sum((k + ps - 1) // ps for k in kv) + 5
+    w = W.make_attention(f"decode_ps{ps}_{d}", [1] * len(kv), kv, 16, 4, d, ps, pool, seed=24, device="cuda",
+                         scales="amax")
+    e, plan = _check(K, oracle, w, chunk_len=chunk_len)
+    print(f"max err {e:.3g}; chunk_len {plan.chunk_len}, chunks {plan.max_chunks}")
