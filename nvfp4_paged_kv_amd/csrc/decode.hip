@@ -183,7 +183,6 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
           ((int64_t)(in_pool ? pg[kb] : 0) * ps + (key - (int)fastdiv((uint32_t)key, a.ps_div) * ps)) *
               a.Hk + hk;
       const int64_t co = rowi * (D / 2) + qq * (C::NQ / 2);
-      const int64_t so = rowi * (D / 16) + qq * (C::NQ / 16);
       if constexpr (C::NC == 4) {
         const u32x4 kw = *(const u32x4*)(a.kc + co), vw = *(const u32x4*)(a.vc + co);
 #pragma unroll
@@ -202,14 +201,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
         r.k[kb][1] = kw.y;
         r.v[kb][0] = vw.x;
         r.v[kb][1] = vw.y;
-        r.ksf[kb] = a.ksf[so];
-        r.vsf[kb] = a.vsf[so];
+        r.ksf[kb] = *(const uint32_t*)(a.ksf + rowi * (D / 16));  // the whole 4-byte scale row
+        r.vsf[kb] = *(const uint32_t*)(a.vsf + rowi * (D / 16));
       }
     }
   };
   // the two E4M3 scales of a quarter (head_dim 64: one, used for both halves)
   auto scales = [&](uint32_t sfw) {
-    const f32x2 s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(C::NC == 4 ? sfw >> (16 * (qq & 1)) : sfw, 1.0f, false);
+    const f32x2 s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(C::NC == 4 ? sfw >> (16 * (qq & 1)) : sfw >> (8 * qq), 1.0f, false);
     return C::NC == 4 ? s : (f32x2){s[0], s[0]};
   };
 
