@@ -356,16 +356,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_merge_kernel(DecodeArgs a)
   if (n <= 1) return;
   constexpr int64_t PF = decode_partial_floats(D);
   constexpr int U = 8;  // chunks whose loads are issued together
-  const float* base = a.partials + item * a.max_chunks * PF;
-  float M = -__builtin_inff();
-  for (int c0 = 0; c0 < n; c0 += U) {
-    float mc[U];
-#pragma unroll
-    for (int i = 0; i < U; ++i) mc[i] = c0 + i < n ? base[(c0 + i) * PF + D] : -__builtin_inff();
-#pragma unroll
-    for (int i = 0; i < U; ++i) M = __builtin_fmaxf(M, mc[i]);
-  }
   constexpr int E = D / 64;
+  const float* base = a.partials + item * a.max_chunks * PF;
+  // Online over blocks of U chunks (one round of loads per block; requests
+  // with at most U chunks need one): the block's max raises the reference,
+  // the running sums are rescaled to it, then the block's chunks are added
+  // in chunk order, so the sums do not depend on the loads' timing.
+  float M = -__builtin_inff();
   float acc[E] = {};
   float L = 0.0f;
   for (int c0 = 0; c0 < n; c0 += U) {
@@ -378,7 +375,16 @@ __global__ __launch_bounds__(64 * kWaves) void decode_merge_kernel(DecodeArgs a)
 #pragma unroll
       for (int e = 0; e < E; ++e) oc[i][e] = base[c * PF + lane * E + e];
     }
-    // in chunk order: the same sums whatever the loads' timing
+    float Mb = M;
+#pragma unroll
+    for (int i = 0; i < U; ++i) Mb = __builtin_fmaxf(Mb, mc[i]);
+    if (c0 > 0 && Mb > M) {  // the reference moves: rescale what is summed
+      const float r = __builtin_amdgcn_exp2f(M - Mb);
+      L *= r;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] *= r;
+    }
+    M = Mb;
 #pragma unroll
     for (int i = 0; i < U; ++i) {
       if (c0 + i >= n) break;
