@@ -228,10 +228,12 @@ def bench_dequant_ablation(K, w, cache, dev_args, out, torch, per_graph=50, repl
     """The 2048x2048 prefill under the three dequant placements of the PR #4769
     page's comparison (graph-timed launches; 4-wave tiles, as the plan picks):
     tiles decoded once per workgroup into f16 LDS (the kernel's own design), K
-    decoded in registers inside the matrix loop, and a byte-table decode."""
+    decoded in registers inside the matrix loop, a byte-table decode, and the
+    f16 design with bf16 staging and bf16 matrix instructions instead."""
     flops = attention_flops(w.q_lens, w.kv_lens, w.num_q_heads, w.head_dim)
     res = {}
-    for mode, name in ((0, "lds_once_per_tile"), (1, "k_in_loop_registers"), (2, "lds_byte_table")):
+    for mode, name in ((0, "lds_once_per_tile"), (1, "k_in_loop_registers"), (2, "lds_byte_table"),
+                       (3, "lds_once_per_tile_bf16")):
         plan = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), w.num_q_heads,
                       w.num_kv_heads, w.head_dim, w.page_size, kv_indptr=torch.from_numpy(w.kv_indptr),
                       tile_waves=4, dequant_mode=mode)

@@ -139,10 +139,14 @@ typedef struct {
        1  K codes and scales staged raw in LDS, every wave decoding its K
           operand fragments in registers inside the matrix loop (V as 0);
        2  as 0, decoding the codes with a byte table (v_perm) instead of the
-          hardware conversion.
-     1 and 2 exist for head_dim 128, GQA group 4, 4-wave tiles (block_q 32)
+          hardware conversion;
+       3  as 0 with a bf16 staging tile, bf16 queries and probabilities and
+          bf16 matrix instructions (0 stages f16: exact as well, fewer
+          instructions).
+     1 to 3 exist for head_dim 128, GQA group 4, 4-wave tiles (block_q 32)
      and page sizes dividing 64; other shapes return NVFP4KV_EUNSUPPORTED.
-     All three give results within the same tolerance of the oracle. */
+     All give results within the same tolerance of the oracle (0, 1 and 2
+     bit-identical). */
   int32_t dequant_mode;
 } nvfp4kv_prefill_plan;
 

@@ -317,7 +317,8 @@ def plan(qo_indptr, kv_lens, num_q_heads, num_kv_heads, head_dim, page_size, kv_
     Q tile (0 automatic, > 0 forced, < 0 never); tile_waves: waves of 32 query
     rows per workgroup (0 automatic, 4 or 8); dequant_mode: the dequant-placement
     ablation (0: tiles decoded once into f16 LDS, the default; 1: K decoded in
-    registers inside the matrix loop; 2: byte-table decode)."""
+    registers inside the matrix loop; 2: byte-table decode; 3: bf16 staging and
+    bf16 matrix instructions)."""
     return Plan(qo_indptr, kv_lens, num_q_heads, num_kv_heads, head_dim, page_size, kv_indptr,
                 l2_bytes, split_len, tile_waves, dequant_mode)
 

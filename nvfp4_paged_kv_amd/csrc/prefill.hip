@@ -41,6 +41,8 @@ namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -146,6 +148,16 @@ constexpr int kSchedMfma = 0x8;
 constexpr int kSchedDsRead = 0x100;
 
 constexpr f16x2 kOnesF16x2 = {(_Float16)1.0f, (_Float16)1.0f};
+constexpr bf16x2 kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // Dequantization kinds (the dequant-placement ablation; 0 is the kernel's own):
 //  0: each KV tile decoded once per workgroup into the f16 staging tile, with
@@ -153,11 +165,37 @@ constexpr f16x2 kOnesF16x2 = {(_Float16)1.0f, (_Float16)1.0f};
 //  1: K codes and scales staged raw, each wave decoding its K fragments in
 //     registers inside the matrix loop (the page's "before" design); V as 0;
 //  2: as 0, with a byte-table decode of the codes instead of the hardware
-//     conversion.
+//     conversion;
+//  3: as 0, with a bf16 staging tile, bf16 queries and probabilities and the
+//     bf16 matrix instructions (the kernel's own 16-bit format is f16).
+// The 16-bit operands travel as raw bits in f16x8 registers either way.
 // Eight codes (one dword) times the f16 scale pair SS, as four f16 pairs.
+// The 32x32x16 matrix instruction on 16-bit operands: f16, or bf16 for the
+// bf16 ablation (DQ 3).
+template <int DQ>
+__device__ __forceinline__ f32x16 mma16(f16x8 a, f16x8 b, f32x16 c) {
+  if constexpr (DQ == 3)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// lo, hi exactly representable in bf16: keep their upper halves
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  return __builtin_amdgcn_perm(f2u(hi), f2u(lo), 0x07060302u);
+}
 template <int DQ>
 __device__ __forceinline__ u32x4 decode8(uint32_t x, f16x2 SS) {
-  if constexpr (DQ != 2) {
+  if constexpr (DQ == 3) {
+    const float S = (float)SS[0];
+    u32x4 r;
+    static_for<0, 4>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const f32x2 f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, j);
+      r[j] = bf16_pair(f[0] * S, f[1] * S);
+    });
+    return r;
+  } else if constexpr (DQ != 2) {
     return (u32x4){fp4x2_times<0>(x, SS), fp4x2_times<1>(x, SS), fp4x2_times<2>(x, SS),
                    fp4x2_times<3>(x, SS)};
   } else {
@@ -303,14 +341,6 @@ __device__ __forceinline__ void pin_jobs(RawJob<D>* job) {
   for (int j = 0; j < Cfg<D, G, W>::JOBS_PER_THREAD; ++j) asm volatile("" : "+v"(job[j].pk), "+v"(job[j].sfrow));
 }
 
-// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
-template <int B, int E, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
 
 // The staging of one KV tile cut into half-words: piece p of a thread
 // dequantizes 8 elements (word (p/2)%4 of job p/8, its low or high half) and
@@ -357,8 +387,8 @@ struct TileStager {
       const _Float16 S = __builtin_bit_cast(f16x2, S01[j])[w < 2 ? 0 : 1];
       const f16x2 SS = {S, S};
       const uint32_t x = job[j].pk[w];
-      if constexpr (DQ == 2) {
-        if constexpr (h == 1) *(u32x4*)(rowp[j] + w * 16) = decode8<2>(x, SS);
+      if constexpr (DQ == 2 || DQ == 3) {
+        if constexpr (h == 1) *(u32x4*)(rowp[j] + w * 16) = decode8<DQ>(x, SS);
       } else {
         chunk[2 * h] = fp4x2_times<2 * h>(x, SS);
         chunk[2 * h + 1] = fp4x2_times<2 * h + 1>(x, SS);
@@ -464,15 +494,17 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
       for (int e = 0; e < 4; ++e) am = max(am, max(qw[c][e] & 0x7FFFu, (qw[c][e] >> 16) & 0x7FFFu));
     }
     am = max(am, (uint32_t)__shfl_xor((int)am, 32));  // the row's other half
-    const int sh = am >= 0x80u ? min(max((int)(am >> 7) - 127 - 14, -100), 113) : 0;
+    const int sh = DQ == 3 ? 0 : am >= 0x80u ? min(max((int)(am >> 7) - 127 - 14, -100), 113) : 0;
     const float down = u2f((uint32_t)(127 - sh) << 23);  // 2^-sh
     cscale = a.sm_scale_log2 * gk * u2f((uint32_t)(127 + sh) << 23);
 #pragma unroll
     for (int c = 0; c < C::NDC; ++c)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const f16x2 h = {(_Float16)(u2f(qw[c][e] << 16) * down), (_Float16)(u2f(qw[c][e] & 0xFFFF0000u) * down)};
-        qw[c][e] = __builtin_bit_cast(uint32_t, h);
+        if constexpr (DQ != 3) {  // (bf16 matrix instructions take the bf16 bits as they are)
+          const f16x2 h = {(_Float16)(u2f(qw[c][e] << 16) * down), (_Float16)(u2f(qw[c][e] & 0xFFFF0000u) * down)};
+          qw[c][e] = __builtin_bit_cast(uint32_t, h);
+        }
       }
 #pragma unroll
     for (int c = 0; c < C::NDC; ++c) __builtin_memcpy(&qf[c], &qw[c], 16);
@@ -544,7 +576,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     TileStager<D, G, W, DQ> stager(job, live, smem + ((jt + 1) & 1) * STG, tid);
     static_for<0, NQK>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[i % KA], qf[i >> 1], s[i & 1], 0, 0, 0);
+      s[i & 1] = mma16<DQ>(kf[i % KA], qf[i >> 1], s[i & 1]);
       if constexpr (i + KA < NQK) kf[i % KA] = kread(i + KA);
       // staging pieces [P0, P1) in this slot
       constexpr int HP = TileStager<D, G, W, DQ>::PIECES;
@@ -603,9 +635,15 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     auto exps = [&](int kc, int j) {  // pair j of chunk kc
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kc >> 1][8 * (kc & 1) + 2 * j], cscale, -m_sub));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kc >> 1][8 * (kc & 1) + 2 * j + 1], cscale, -m_sub));
-      const f16x2 pp = {(_Float16)p0, (_Float16)p1};
-      l_run = __builtin_amdgcn_fdot2(pp, kOnesF16x2, l_run, false);
-      pw[kc][j] = __builtin_bit_cast(uint32_t, pp);
+      if constexpr (DQ == 3) {
+        const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnesBf16x2, l_run, false);
+        pw[kc][j] = __builtin_bit_cast(uint32_t, pp);
+      } else {
+        const f16x2 pp = {(_Float16)p0, (_Float16)p1};
+        l_run = __builtin_amdgcn_fdot2(pp, kOnesF16x2, l_run, false);
+        pw[kc][j] = __builtin_bit_cast(uint32_t, pp);
+      }
     };
     auto vread = [&](int i) {  // MFMA i: chunk i / NDB, head_dim block i % NDB
       const uint8_t* vp = vbase + (i / C::NDB) * 16 * C::VROW + (i % C::NDB) * 64;
@@ -627,7 +665,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
       constexpr int kc = i / C::NDB, db = i % C::NDB;
       f16x8 pf;
       __builtin_memcpy(&pf, pw[kc], 16);
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[i % VA], pf, o[db], 0, 0, 0);
+      o[db] = mma16<DQ>(vf[i % VA], pf, o[db]);
       if constexpr (i + VA < NPV) vf[i % VA] = vread(i + VA);
       if constexpr (kc + 1 < 4) {
         // pairs [J0, J1) of chunk kc+1 in this slot
@@ -917,13 +955,15 @@ extern "C" int paged_prefill_causal(const void* q, const int32_t* qo_indptr,
   if (p.dequant_mode != 0) {
     // dequant-placement ablation: head_dim 128, GQA group 4, 4-wave tiles,
     // page sizes dividing the KV tile
-    if (D != 128 || G != 4 || W != 4 || kBlockN % c.page_size != 0 ||
-        (p.dequant_mode != 1 && p.dequant_mode != 2))
+    if (D != 128 || G != 4 || W != 4 || kBlockN % c.page_size != 0 || p.dequant_mode < 1 ||
+        p.dequant_mode > 3)
       return NVFP4KV_EUNSUPPORTED;
     if (p.dequant_mode == 1)
       hipLaunchKernelGGL((prefill_kernel<128, 4, 4, true, 1>), dim3(a.num_items), dim3(256), 0, s, a);
-    else
+    else if (p.dequant_mode == 2)
       hipLaunchKernelGGL((prefill_kernel<128, 4, 4, true, 2>), dim3(a.num_items), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<128, 4, 4, true, 3>), dim3(a.num_items), dim3(256), 0, s, a);
     return hipGetLastError() == hipSuccess ? NVFP4KV_OK : NVFP4KV_EHIP;
   }
 #define NVFP4KV_CASE(DD, GG, WW) \

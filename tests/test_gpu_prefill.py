@@ -215,6 +215,38 @@ def test_prefill_dequant_ablation_modes(K, oracle, mode):
     assert_close(out.index_select(0, torch.from_numpy(rows).cuda()), ref, w.name)
 
 
+def test_prefill_bf16_staging_mode(K, oracle):
+    """The bf16 variant of the kernel (bf16 staging tile, queries and
+    probabilities, bf16 matrix instructions) against the oracle."""
+    banner("prefill bf16 staging (dequant mode 3)")
+    q = [1, 37, 200, 64, 3, 129]
+    kv = [1, 37, 333, 700, 3, 130]
+    w = W.make_attention("dequant_mode_3", q, kv, 32, 8, 128, 16, 120, seed=19, device="cuda",
+                         scales="amax")
+    plan = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), 32, 8, 128, 16,
+                  kv_indptr=torch.from_numpy(w.kv_indptr), split_len=2, tile_waves=4,
+                  dequant_mode=3)
+    assert plan.num_split_tiles > 0
+    out, _, _ = run_gpu(K, w, plan=plan)
+    torch.cuda.synchronize()
+    assert K.read_device_error("cuda") == 0
+    ref, rows = oracle_outputs(oracle, w)
+    assert_close(out.index_select(0, torch.from_numpy(rows).cuda()), ref, w.name)
+
+
+def test_prefill_bf16_staging_2k(K, oracle):
+    """The bf16 variant on the full 2048x2048 batch."""
+    banner("prefill bf16 staging, 2048x2048")
+    w = W.prefill_2k("cuda")
+    plan = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), 32, 8, 128, 16,
+                  kv_indptr=torch.from_numpy(w.kv_indptr), tile_waves=4, dequant_mode=3)
+    out, _, _ = run_gpu(K, w, plan=plan)
+    torch.cuda.synchronize()
+    assert K.read_device_error("cuda") == 0
+    ref, rows = oracle_outputs(oracle, w)
+    assert_close(out.index_select(0, torch.from_numpy(rows).cuda()), ref, w.name)
+
+
 def test_prefill_dequant_ablation_unsupported_shape(K):
     """The ablation kernels exist for head_dim 128, GQA group 4, 4-wave tiles
     only: other shapes are refused before any launch."""
