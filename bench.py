@@ -189,11 +189,12 @@ def main():
         result["dequant_ablation"] = bench_dequant_ablation(K, w, cache, (qo_d, kvp_d, pt_d, kvl_d), out,
                                                             torch)
     if not args.no_achievable:
-        ach = bench_achievable(dev, torch, np)
+        ach = bench_achievable(W, dev, torch, np)
         ach["prefill_frac_of_mfma_loop"] = round(pre_tflops / ach["mfma_bf16_TFLOPs"], 4)
         if "append_stress" in result:
-            ach["append_stress_frac_of_copy"] = round(
-                result["append_stress"]["achieved_GBps"] / ach["copy_GBps"], 4)
+            got = result["append_stress"]["achieved_GBps"]
+            ach["append_stress_frac_of_copy"] = round(got / ach["copy_GBps"], 4)
+            ach["append_stress_frac_of_traffic_probe"] = round(got / ach["append_traffic_GBps"], 4)
         result["achievable"] = ach
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, flops)
@@ -340,21 +341,32 @@ def bench_decode(K, W, dev, torch, np, iters=12):
             "chunk_len": plan.chunk_len, "cache": "cold (flushed)", "traffic": _traffic("decode")}
 
 
-def bench_achievable(dev, torch, np):
-    """Measured achievable peaks on this device: a plain 256 MiB device copy
-    (read + write bytes / time) and the MFMA-only loop of peak.hip (dense
-    v_mfma_f32_32x32x16_bf16, two waves per SIMD); medians of 10 launches,
-    HIP events on the launch stream."""
+def bench_achievable(W, dev, torch, np):
+    """Measured achievable rates on this device.  Cold, like the append and
+    decode figures (the 256 MB Infinity Cache flushed by an untimed 512 MiB
+    read before every launch; median of 12 launches, HIP events on the launch
+    stream): a 16-byte-per-lane copy of 128 MiB (read + write bytes / time),
+    and the 65,536-token append's own data movement without its arithmetic
+    (peak.hip append_traffic: the same bf16 loads and the same code and
+    scale stores through the same scattered slots; the append's algorithmic
+    bytes / time).  Warm: the MFMA-only loop of peak.hip (dense
+    v_mfma_f32_32x32x16_bf16, two waves per SIMD; median of 10)."""
     import ctypes
     from nvfp4_paged_kv_amd.build import PEAK_LIB
-    src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
+    if not os.path.exists(PEAK_LIB):
+        raise SystemExit(f"{PEAK_LIB} missing: run __graft_entry__.build()")
+    L = ctypes.CDLL(PEAK_LIB)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    vp = ctypes.c_void_p
+    flush = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
 
-    def timed(fn, n=10):
+    def timed(fn, n=10, cold=False):
         for _ in range(3):
             fn()
         ts = []
         for _ in range(n):
+            if cold:
+                torch.amax(flush)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             fn()
@@ -363,17 +375,36 @@ def bench_achievable(dev, torch, np):
             ts.append(e0.elapsed_time(e1) * 1e-3)
         return float(np.median(ts))
 
-    copy_s = timed(lambda: dst.copy_(src))
+    def check(rc, what):
+        if rc != 0:
+            raise SystemExit(f"{what} probe launch failed")
+
+    src = torch.ones(128 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    L.nvfp4kv_copy_probe.argtypes = [vp, vp, ctypes.c_int64, vp]
+    copy_s = timed(lambda: check(L.nvfp4kv_copy_probe(vp(src.data_ptr()), vp(dst.data_ptr()),
+                                                      src.numel() // 16, stream), "copy"), n=12, cold=True)
     out = {"copy_GBps": round(2 * src.numel() / copy_s / 1e9, 1)}
-    if not os.path.exists(PEAK_LIB):
-        raise SystemExit(f"{PEAK_LIB} missing: run __graft_entry__.build()")
-    L = ctypes.CDLL(PEAK_LIB)
+    del src, dst
+
+    a = W.append_stress(dev)
+    cache = [torch.empty((a.num_pages, a.page_size, a.num_kv_heads, a.head_dim // d), dtype=torch.uint8,
+                         device=dev) for d in (2, 2, 16, 16)]
+    L.nvfp4kv_append_traffic_probe.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int64, vp, vp, vp, vp, vp]
+    traffic_s = timed(lambda: check(L.nvfp4kv_append_traffic_probe(
+        vp(a.k.data_ptr()), vp(a.v.data_ptr()), vp(a.slot_mapping.data_ptr()), a.k.shape[0],
+        a.num_kv_heads, a.head_dim, a.num_pages * a.page_size, *(vp(c.data_ptr()) for c in cache),
+        stream), "append traffic"), n=12, cold=True)
+    out["append_traffic_GBps"] = round(append_bytes(a.k.shape[0], a.num_kv_heads, a.head_dim)
+                                       / traffic_s / 1e9, 1)
+    del a, cache, flush
+
     L.nvfp4kv_mfma_peak_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     L.nvfp4kv_mfma_peak_probe_flops.restype = ctypes.c_double
     L.nvfp4kv_mfma_peak_probe_flops.argtypes = [ctypes.c_int, ctypes.c_int]
     blocks, iters = 256 * 4, 2000
     buf = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
     def mfma():
         if L.nvfp4kv_mfma_peak_probe(blocks, iters, ctypes.c_void_p(buf.data_ptr()), stream) != 0:

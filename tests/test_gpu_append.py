@@ -1,5 +1,5 @@
-"""GPU parity of the NVFP4 append (bit-exact against the oracle) and its
-boundary behaviour: device scale checks (eager and graph replay), zero rows,
+"""GPU parity of the NVFP4 append (bit-exact against the oracle; both the
+two-block and the half-block kernels) and its boundary behaviour: device scale checks (eager and graph replay), zero rows,
 padding / out-of-range slots, and no host synchronization."""
 import numpy as np
 import pytest
@@ -81,6 +81,24 @@ def test_append_bitexact_special_values(K, oracle):
     P, ps = 8, 16
     slots = torch.randperm(P * ps, generator=g)[:T].to(torch.int64).cuda()
     for ks, vs in [(1.0, 1.0), (1e-30, 7.5), (3.0e33, 1e-5), (2.0 ** -149, 1.0e38)]:
+        cache = _gpu_append(K, k, v, slots, ks, vs, P, ps)
+        ref, oerr = _oracle_cache(oracle, k, v, slots, ks, vs, P, ps)
+        assert oerr == 0
+        _compare(cache, ref)
+
+
+@pytest.mark.parametrize("H,D", [(1, 16), (3, 48), (2, 48), (5, 32)])
+def test_append_bitexact_block_counts(K, oracle, H, D):
+    """Token rows with an odd number of 16-element blocks (the half-block
+    kernel: H=1 D=16, H=3 D=48) and with an even number whose two-block units
+    straddle head boundaries (H=2 D=48, H=5 D=32)."""
+    banner(f"append bit-exact H={H} D={D}")
+    g = torch.Generator().manual_seed(11 + H * D)
+    T, P, ps = 77, 8, 16
+    k = torch.randn(T, H, D, generator=g).to(torch.bfloat16).cuda()
+    v = (torch.randn(T, H, D, generator=g) * 3).to(torch.bfloat16).cuda()
+    slots = torch.randperm(P * ps, generator=g)[:T].to(torch.int64).cuda()
+    for ks, vs in [(1.0, 1.0), (0.01, 0.2)]:
         cache = _gpu_append(K, k, v, slots, ks, vs, P, ps)
         ref, oerr = _oracle_cache(oracle, k, v, slots, ks, vs, P, ps)
         assert oerr == 0
