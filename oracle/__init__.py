@@ -83,7 +83,7 @@ def _ptr(a: np.ndarray):
 
 
 def _threads() -> int:
-    # at most 16 worker threads (the CPU share of a one-GPU machine)
+    # at most 16 worker threads
     return max(1, min(os.cpu_count() or 1, 16))
 
 
