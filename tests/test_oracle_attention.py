@@ -282,3 +282,64 @@ def test_prefill_sampled_requests_and_errors(oracle):
     _, err = oracle.prefill(W.bf16_bits(w.q), w.qo_indptr, w.kv_indptr, bad_pt, w.kv_lens, *caches,
                             w.k_scale, w.v_scale, w.num_q_heads, w.sm_scale)
     assert err & 8
+
+
+def _flash_rows(q, K, V, sm_scale, nkeys, block, slack, chunks):
+    """fp64 online softmax over the allowed keys of each row, in `block`-key
+    tiles, with the reference max raised only when a tile's max exceeds it by
+    more than `slack` (log2 units), the key range cut into `chunks` pieces
+    whose (unnormalized O, max, sum) are merged in chunk order: the regrouping
+    the prefill and decode kernels use (reading R26), written independently of
+    the oracle."""
+    out = np.zeros((q.shape[0], V.shape[1]))
+    c = sm_scale / np.log(2.0)  # scores -> log2 domain
+    for i in range(q.shape[0]):
+        n = nkeys[i]
+        bounds = [n * t // chunks for t in range(chunks + 1)]
+        parts = []
+        for a, b in zip(bounds[:-1], bounds[1:]):
+            m, l, o = -np.inf, 0.0, np.zeros(V.shape[1])
+            for t0 in range(a, b, block):
+                s = (K[t0:min(t0 + block, b)] @ q[i]) * c
+                mt = s.max()
+                if mt > m + slack:  # lazy: raise the reference max only on large growth
+                    alpha = np.exp2(m - mt) if m > -np.inf else 0.0
+                    o *= alpha
+                    l *= alpha
+                    m = mt
+                p = np.exp2(s - m)
+                l += p.sum()
+                o += p @ V[t0:min(t0 + block, b)]
+            parts.append((m, l, o))
+        mall = max(pm for pm, _, _ in parts if pm > -np.inf)
+        L = sum(pl * np.exp2(pm - mall) for pm, pl, _ in parts if pm > -np.inf)
+        O = sum(po * np.exp2(pm - mall) for pm, _, po in parts if pm > -np.inf)
+        out[i] = O / L
+    return out
+
+
+@pytest.mark.parametrize("block,slack,chunks", [(64, 8.0, 1), (48, 8.0, 3), (7, 0.0, 2), (64, 8.0, 5)])
+def test_online_softmax_regrouping_matches_definition(oracle, block, slack, chunks):
+    """Tiled online softmax with lazy rescaling and chunk merging (the kernels'
+    algorithm, in fp64) equals the oracle's plain definition to 1e-12, with
+    tile sizes that do not divide the lengths and chunks that may be empty of
+    tiles; scores are scaled up (std 4) so that the lazy max does lag."""
+    w = small(11, q=(1, 37, 70), kv=(3, 90, 70), std=4.0)
+    caches = fill(oracle, w)
+    ref = run_oracle(oracle, w, caches)
+    K = decode_numpy(caches[0], caches[2], w.k_scale)
+    V = decode_numpy(caches[1], caches[3], w.v_scale)
+    q = w.q.double().numpy()
+    G = w.num_q_heads // w.num_kv_heads
+    for r in range(w.batch):
+        Lq, Lk = int(w.q_lens[r]), int(w.kv_lens[r])
+        pages = w.page_table[w.kv_indptr[r]:w.kv_indptr[r + 1]]
+        j = np.arange(Lk)
+        Kr = K[pages[j // w.page_size], j % w.page_size]
+        Vr = V[pages[j // w.page_size], j % w.page_size]
+        nkeys = Lk - Lq + np.arange(Lq) + 1
+        rows = slice(w.qo_indptr[r], w.qo_indptr[r + 1])
+        for hq in range(w.num_q_heads):
+            got = _flash_rows(q[rows, hq], Kr[:, hq // G], Vr[:, hq // G], w.sm_scale, nkeys, block,
+                              slack, chunks)
+            np.testing.assert_allclose(got, ref[rows, hq], rtol=1e-12, atol=1e-13)
