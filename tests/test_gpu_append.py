@@ -87,6 +87,22 @@ def test_append_bitexact_special_values(K, oracle):
         _compare(cache, ref)
 
 
+def test_append_bitexact_uniform_1k_full(K, oracle):
+    """The largest append: 1024 requests x 1024 tokens (1,048,576 rows, 2 GiB
+    of bf16 per tensor, 65,536 pages, lognormal global scales), every byte of
+    the GPU caches against the oracle's."""
+    banner("append bit-exact uniform 1024x1024 (1M tokens)")
+    w = W.uniform_batch_1k("cuda")
+    err = K.device_error_word("cuda")
+    err.zero_()
+    cache = _gpu_append(K, w.k, w.v, w.slot_mapping, w.k_scale, w.v_scale, w.num_pages, w.page_size, err)
+    assert K.read_device_error("cuda") == 0
+    ref, oerr = _oracle_cache(oracle, w.k, w.v, w.slot_mapping, w.k_scale, w.v_scale, w.num_pages,
+                              w.page_size)
+    assert oerr == 0
+    _compare(cache, ref)
+
+
 @pytest.mark.parametrize("H,D", [(1, 16), (3, 48), (2, 48), (5, 32)])
 def test_append_bitexact_block_counts(K, oracle, H, D):
     """Token rows with an odd number of 16-element blocks (the half-block
