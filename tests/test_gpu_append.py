@@ -87,12 +87,14 @@ def test_append_bitexact_special_values(K, oracle):
         _compare(cache, ref)
 
 
-def test_append_bitexact_uniform_1k_full(K, oracle):
-    """The largest append: 1024 requests x 1024 tokens (1,048,576 rows, 2 GiB
-    of bf16 per tensor, 65,536 pages, lognormal global scales), every byte of
-    the GPU caches against the oracle's."""
-    banner("append bit-exact uniform 1024x1024 (1M tokens)")
-    w = W.uniform_batch_1k("cuda")
+@pytest.mark.parametrize("name", ["uniform_batch_1k", "ragged_chunked"])
+def test_append_bitexact_large_batches(K, oracle, name):
+    """The largest appends, every byte of the GPU caches against the oracle's:
+    1024 requests x 1024 tokens (1,048,576 rows, 2 GiB of bf16 per tensor,
+    65,536 pages, lognormal global scales), and the ragged batch's whole cache
+    (256 requests, kv_len ~ U[1, 4096], permuted pages)."""
+    banner(f"append bit-exact {name}")
+    w = getattr(W, name)("cuda")
     err = K.device_error_word("cuda")
     err.zero_()
     cache = _gpu_append(K, w.k, w.v, w.slot_mapping, w.k_scale, w.v_scale, w.num_pages, w.page_size, err)
