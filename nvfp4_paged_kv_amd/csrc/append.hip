@@ -25,6 +25,8 @@
 namespace nvfp4kv {
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return u2f(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return u2f(w & 0xFFFF0000u); }
 
@@ -124,7 +126,10 @@ __global__ __launch_bounds__(256) void append_kernel(
   const uint32_t token = fastdiv(h, hpt);
   const uint32_t j = h - token * hpt.d;  // half block within the token row
   const int64_t slot = slots[token];
-  const uint4 kx = k[h], vx = v[h];
+  // the bf16 rows are read once: streaming (non-temporal) loads
+  const u32x4 kr = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k) + h);
+  const u32x4 vr = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v) + h);
+  const uint4 kx = make_uint4(kr[0], kr[1], kr[2], kr[3]), vx = make_uint4(vr[0], vr[1], vr[2], vr[3]);
   uint32_t ksf, vsf;
   const uint32_t kp = quantize_half(kx, gk, 6.0f * gk, ksf);
   const uint32_t vp = quantize_half(vx, gv, 6.0f * gv, vsf);
@@ -135,9 +140,11 @@ __global__ __launch_bounds__(256) void append_kernel(
   }
   // NHD: the cache row of a slot is [slot][H_kv][D/2] bytes (4 per half
   // block), its scale row [slot][H_kv][D/16] (1 per block).
+  // Plain (write-back) stores: the scattered 512-byte rows merge in L2
+  // (streaming stores measured ~2% slower here).
   const size_t o = (size_t)slot * hpt.d + j;
-  __builtin_nontemporal_store(kp, &k_cache[o]);
-  __builtin_nontemporal_store(vp, &v_cache[o]);
+  k_cache[o] = kp;
+  v_cache[o] = vp;
   if ((j & 1) == 0) {
     k_sf[o >> 1] = (uint8_t)ksf;
     v_sf[o >> 1] = (uint8_t)vsf;
