@@ -12,6 +12,7 @@
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kAcc = 8;  // independent accumulators per wave
@@ -46,7 +47,8 @@ __global__ __launch_bounds__(256) void copy16(const uint4* __restrict__ a, uint4
 
 // One thread per 8 bf16 of K and of V (the append's half blocks): loads them,
 // folds each 16 bytes into a 4-byte word (no quantization), and stores the
-// words and one byte per even lane where the append stores codes and scales.
+// words and one byte per even lane where the append stores codes and scales,
+// with the append's cache hints.
 __global__ __launch_bounds__(256) void append_traffic(const uint4* __restrict__ k, const uint4* __restrict__ v,
                                                       const int64_t* __restrict__ slots, int64_t n, int hpt,
                                                       int64_t num_slots, uint32_t* __restrict__ kc,
@@ -57,12 +59,14 @@ __global__ __launch_bounds__(256) void append_traffic(const uint4* __restrict__ 
   const int64_t token = h / hpt;
   const int j = (int)(h - token * hpt);
   const int64_t slot = slots[token];
-  const uint4 x = k[h], y = v[h];
+  // the append's cache hints: streaming loads, write-back stores
+  const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k) + h);
+  const u32x4 y = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v) + h);
   if (slot < 0 || slot >= num_slots) return;
-  const uint32_t a = x.x ^ x.y ^ x.z ^ x.w, b = y.x ^ y.y ^ y.z ^ y.w;
+  const uint32_t a = x[0] ^ x[1] ^ x[2] ^ x[3], b = y[0] ^ y[1] ^ y[2] ^ y[3];
   const int64_t o = slot * hpt + j;
-  __builtin_nontemporal_store(a, &kc[o]);
-  __builtin_nontemporal_store(b, &vc[o]);
+  kc[o] = a;
+  vc[o] = b;
   if ((j & 1) == 0) {
     ks[o >> 1] = (uint8_t)a;
     vs[o >> 1] = (uint8_t)b;
