@@ -796,17 +796,111 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
 // exclusive scan in descending cost order, then each (request, Q tile) pair,
 // one per thread, places its items (x KV heads) at the next free positions of
 // their cost buckets.  An item is a Q tile, or, when split_len > 0, one of
-// the balanced chunks of its KV range.
+// the balanced chunks of its KV range.  Batches whose KV does not fit in L2
+// (PR #3575 page, section 3) use the stream order below instead.
 constexpr int kCostBuckets = 4096;
 
 __device__ __forceinline__ int tile_cost(int lq, int off, int t, int BQ) {
   return (off + min((t + 1) * BQ, lq) - 1) / kBlockN + 1;
 }
 
+// Exclusive scan of `sum` (this thread's share) across the 1024 threads:
+// returns the sum of the shares of threads 0 .. tid-1.
+__device__ __forceinline__ int block_exclusive_scan(int sum, int* warp_tot) {
+  const int tid = threadIdx.x;
+  int incl = sum;
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(incl, o);
+    if ((tid & 63) >= o) incl += y;
+  }
+  if ((tid & 63) == 63) warp_tot[tid >> 6] = incl;
+  __syncthreads();
+  int wbase = 0;
+  for (int w = 0; w < (tid >> 6); ++w) wbase += warp_tot[w];
+  __syncthreads();
+  return wbase + incl - sum;
+}
+
+// Stream order (large batches whose KV does not fit in L2, nothing split):
+// requests sorted by total cost, heaviest first; the Q tiles of one (request,
+// KV head) stream consecutive and heaviest first, all on one XCD (workgroup p
+// runs on XCD p % 8, and the stream of head h goes to XCD h % 8), so that a
+// stream's KV tiles are fetched once into that XCD's L2 and reused by its Q
+// tiles while they are resident.  Needs Hk % 8 == 0 (every XCD then gets the
+// same number of items) and B <= kStreamOrderMaxReq.
+constexpr int kStreamOrderMaxReq = 8192;
+constexpr int kXcds = 8;
+
+__device__ void worklist_stream_order(const int32_t* __restrict__ qo, const int32_t* __restrict__ kvl,
+                                      int B, int Hk, int BQ, int QT, int4* __restrict__ list,
+                                      int* hist, int* warp_tot) {
+  __shared__ int rank_req[kStreamOrderMaxReq];  // request of each rank
+  __shared__ int rank_off[kStreamOrderMaxReq];  // tiles of the rank, then their exclusive scan
+  const int tid = threadIdx.x;
+  auto ntiles_of = [&](int rq) { return (qo[rq + 1] - qo[rq] + BQ - 1) / BQ; };
+  auto total_of = [&](int rq) {
+    const int lq = qo[rq + 1] - qo[rq], off = kvl[rq] - lq;
+    int tot = 0;
+    for (int t = 0; t * BQ < lq; ++t) tot += tile_cost(lq, off, t, BQ);
+    return tot;
+  };
+  for (int rq = tid; rq < B; rq += 1024) atomicAdd(&hist[min(total_of(rq), kCostBuckets - 1)], 1);
+  __syncthreads();
+  // bucket starts in descending total cost
+  constexpr int per = kCostBuckets / 1024;
+  int vals[per], sum = 0;
+  for (int i = 0; i < per; ++i) {
+    vals[i] = hist[kCostBuckets - 1 - (tid * per + i)];
+    sum += vals[i];
+  }
+  int run = block_exclusive_scan(sum, warp_tot);
+  for (int i = 0; i < per; ++i) {
+    hist[kCostBuckets - 1 - (tid * per + i)] = run;
+    run += vals[i];
+  }
+  __syncthreads();
+  for (int rq = tid; rq < B; rq += 1024) {
+    const int rank = atomicAdd(&hist[min(total_of(rq), kCostBuckets - 1)], 1);
+    rank_req[rank] = rq;
+    rank_off[rank] = ntiles_of(rq);
+  }
+  __syncthreads();
+  // exclusive scan of the tile counts in rank order
+  constexpr int rper = kStreamOrderMaxReq / 1024;
+  int rv[rper], rsum = 0;
+  for (int i = 0; i < rper; ++i) {
+    const int rank = tid * rper + i;
+    rv[i] = rank < B ? rank_off[rank] : 0;
+    rsum += rv[i];
+  }
+  int rrun = block_exclusive_scan(rsum, warp_tot);
+  for (int i = 0; i < rper; ++i) {
+    const int rank = tid * rper + i;
+    if (rank < B) rank_off[rank] = rrun;
+    rrun += rv[i];
+  }
+  __syncthreads();
+  // XCD x holds heads h = x, x + 8, ...: per rank, Hk/8 streams of nt tiles
+  const int hpx = Hk / kXcds;
+  for (int rank = tid; rank < B; rank += 1024) {
+    const int rq = rank_req[rank];
+    const int lq = qo[rq + 1] - qo[rq], off = kvl[rq] - lq;
+    const int nt = ntiles_of(rq);
+    for (int h = 0; h < Hk; ++h) {
+      const int x = h % kXcds, hi = h / kXcds;
+      for (int tp = 0; tp < nt; ++tp) {
+        const int t = nt - 1 - tp;  // heaviest tile first
+        const int local = rank_off[rank] * hpx + hi * nt + tp;
+        list[(int64_t)local * kXcds + x] = make_int4(rq, t * Hk + h, tile_cost(lq, off, t, BQ), -1);
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(1024) void worklist_kernel(const int32_t* __restrict__ qo,
                                                         const int32_t* __restrict__ kvl, int B,
                                                         int Hk, int BQ, int QT, int split_len,
-                                                        int4* __restrict__ list) {
+                                                        int stream_order, int4* __restrict__ list) {
   __shared__ int hist[kCostBuckets];
   __shared__ int warp_tot[16];
   __shared__ int n_split;
@@ -814,6 +908,10 @@ __global__ __launch_bounds__(1024) void worklist_kernel(const int32_t* __restric
   for (int i = tid; i < kCostBuckets; i += 1024) hist[i] = 0;
   if (tid == 0) n_split = 0;
   __syncthreads();
+  if (stream_order) {
+    worklist_stream_order(qo, kvl, B, Hk, BQ, QT, list, hist, warp_tot);
+    return;
+  }
   for (int64_t i = tid; i < (int64_t)B * QT; i += 1024) {
     const int rq = (int)(i / QT), t = (int)(i - (int64_t)rq * QT);
     const int lq = qo[rq + 1] - qo[rq], off = kvl[rq] - lq;
@@ -945,8 +1043,12 @@ extern "C" int paged_prefill_causal(const void* q, const int32_t* qo_indptr,
     a.partials = (float*)((uint8_t*)workspace + wl.partials);
     a.partial_floats = wl.partial_bytes / 4;
     a.max_chunks = p.max_chunks;
+    // stream order when the KV working set does not fit in L2 and nothing is
+    // split (otherwise: every item heaviest first)
+    const int stream_order = !p.head_first && p.split_len == 0 && p.num_kv_heads % kXcds == 0 &&
+                             p.batch <= kStreamOrderMaxReq;
     hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(1024), 0, s, qo_indptr, kv_lens, p.batch,
-                       p.num_kv_heads, p.block_q, p.q_tiles_per_head, p.split_len,
+                       p.num_kv_heads, p.block_q, p.q_tiles_per_head, p.split_len, stream_order,
                        (int4*)workspace);
   }
   const int G = p.num_q_heads / p.num_kv_heads;
