@@ -293,11 +293,20 @@ class Plan:
         n = self.struct.workspace_bytes
         if n == 0:
             return None
-        device = torch.device(device)
+        device = _norm_device(device)
         if device not in self._workspace:
             # zero-filled once (a fill kernel); the kernels leave it zeroed
             self._workspace[device] = torch.zeros(n, dtype=torch.uint8, device=device)
         return self._workspace[device]
+
+
+def _norm_device(device) -> torch.device:
+    """torch.device with the current GPU's index filled in, so that "cuda" and
+    "cuda:N" name one workspace."""
+    device = torch.device(device)
+    if device.type == "cuda" and device.index is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    return device
 
 
 def _host_int32(t, name) -> torch.Tensor:
@@ -380,7 +389,7 @@ class DecodePlan:
         n = self.struct.workspace_bytes
         if n == 0:
             return None
-        device = torch.device(device)
+        device = _norm_device(device)
         if device not in self._workspace:
             self._workspace[device] = torch.empty(n, dtype=torch.uint8, device=device)
         return self._workspace[device]

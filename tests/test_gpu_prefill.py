@@ -170,6 +170,56 @@ def test_schedule_orders_give_identical_bits(K):
         assert torch.equal(o, base)
 
 
+def test_stream_ordered_work_list_layout(K):
+    """The work list of a ragged batch whose KV is taken not to fit in L2:
+    every (request, Q tile, KV head) item exactly once; position p holds a
+    stream of head h only when p % 8 == h % 8 (workgroup p runs on XCD p % 8);
+    a stream's items are consecutive in its XCD's sequence, heaviest tile
+    first; requests appear in non-increasing total cost."""
+    banner("stream-ordered work list layout")
+    q_lens = [37, 512, 1, 200, 64, 300, 129, 5]
+    kv_lens = [900, 3000, 40, 200, 2500, 1700, 129, 4000]
+    w = W.make_attention("wl", q_lens, kv_lens, 32, 8, 128, 16, 800, seed=17, device="cuda",
+                         scales="amax")
+    plan = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), 32, 8, 128, 16,
+                  split_len=-1, tile_waves=8)
+    plan.struct.head_first = 0
+    out, cache, plan = run_gpu(K, w, plan=plan)
+    torch.cuda.synchronize()
+    n = plan.num_items
+    lst = plan.workspace("cuda")[: n * 16].view(torch.int32).view(n, 4).cpu().numpy()
+    bq, hk = plan.block_q, 8
+
+    def cost(r, t):
+        lq, off = int(w.q_lens[r]), int(w.kv_lens[r] - w.q_lens[r])
+        return (off + min((t + 1) * bq, lq) - 1) // 64 + 1
+
+    seen = set()
+    for p, (r, y, z, sp) in enumerate(lst):
+        t, h = divmod(int(y), hk)
+        assert sp == -1 and z == cost(r, t)
+        assert p % 8 == h % 8
+        seen.add((int(r), t, h))
+    expect = {(r, t, h) for r in range(w.batch) for t in range(-(-int(w.q_lens[r]) // bq)) for h in range(hk)}
+    assert seen == expect and len(seen) == n
+    totals = []
+    for x in range(8):
+        seq = lst[x::8]
+        run = []
+        for r, y, _, _ in seq:
+            t, h = divmod(int(y), hk)
+            if run and run[-1][0] == (r, h):
+                assert t == run[-1][1] - 1  # consecutive, heaviest first
+                run[-1][1] = t
+            else:
+                assert not any(k == (r, h) for k, _ in run)  # a stream appears once
+                assert t == -(-int(w.q_lens[r]) // bq) - 1
+                run.append([(r, h), t])
+        if x == 0:
+            totals = [sum(cost(r, t) for t in range(-(-int(w.q_lens[r]) // bq))) for (r, h), _ in run]
+    assert all(a >= b for a, b in zip(totals, totals[1:]))
+
+
 def test_page_id_out_of_range_sets_flag(K):
     w = W.tiny("cuda")
     out, cache, plan = run_gpu(K, w)
