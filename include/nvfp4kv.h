@@ -118,7 +118,8 @@ typedef struct {
   int64_t total_q, total_kv;
   int32_t uniform_q;   /* [PR #3575] review: total_q == batch * max_q_len */
   int32_t uniform_kv;  /* total_kv == batch * max_kv_len (informational) */
-  int32_t head_first;  /* [PR #3575] L2 gate: all KV streams fit in L2 */
+  int32_t head_first;  /* [PR #3575] L2 gate: all KV streams fit in L2 (informational;
+                          `schedule` is what runs) */
   int32_t block_q;     /* query tokens per tile (tile = block_q tokens x G heads) */
   int32_t block_n;     /* keys per KV tile */
   int32_t q_tiles_per_head; /* uniform: ceil(max_q_len / block_q) */
@@ -148,6 +149,21 @@ typedef struct {
      All give results within the same tolerance of the oracle (0, 1 and 2
      bit-identical). */
   int32_t dequant_mode;
+  int32_t cu_count;         /* CUs the tile width and the KV split were sized for */
+  /* Order in which the Q tiles (or their KV chunks) are issued.  The plan
+     fills in its own choice; a caller may change it before
+     paged_prefill_causal (results are bitwise the same in every order):
+       1  heaviest first over every request and head ([PR #3575] sections 1
+          and 2: global reverse order; head-first when the KV fits in L2);
+       2  stream order: the Q tiles of one (request, KV head) consecutive,
+          heaviest first, all on one XCD (the plan's choice when the KV does
+          not fit in L2, [PR #3575] section 3); not with split Q tiles, and
+          for ragged batches only with num_kv_heads % 8 == 0 and batch <= 8192;
+       3  request order: requests in order, each one's Q tiles lightest first
+          (no reordering; the baseline the other two are measured against).
+     Other values, or 2 where it is not available, return
+     NVFP4KV_EUNSUPPORTED. */
+  int32_t schedule;
 } nvfp4kv_prefill_plan;
 
 /*
@@ -162,7 +178,9 @@ typedef struct {
  *   kv_indptr_host  int32 [batch+1] or NULL: if given, each request must own
  *                   exactly ceil(kv_len / page_size) page-table entries.
  *   l2_bytes        L2 capacity of the whole device for the gate; 0 = query
- *                   the current HIP device (and its CU count).
+ *                   the current HIP device.
+ *   cu_count        compute units to size the tile width and the KV split
+ *                   for; 0 = query the current HIP device.
  *   split_len       KV tiles per chunk when heavy Q tiles are split: 0 =
  *                   automatic (only for batches whose Q tiles cannot fill
  *                   every workgroup slot of the GPU), > 0 = split every Q
@@ -173,19 +191,27 @@ typedef struct {
  * Returns NVFP4KV_ERANGE if some q_len > kv_len, a length is negative, or a
  * page count does not match; NVFP4KV_EUNSUPPORTED if head_dim is not 64 or
  * 128, or num_q_heads / num_kv_heads is not 1, 2, 4 or 8; NVFP4KV_EINVAL for
- * a tile_waves other than 0, 4 or 8 (8 with head_dim 64).
+ * a tile_waves other than 0, 4 or 8 (8 with head_dim 64), or a negative
+ * l2_bytes or cu_count.
+ * The reductions are single passes over the two int32 arrays in compiled
+ * code (the work of a whole-tensor reduction, without a per-element
+ * interpreted loop); only batches small enough to have their KV ranges split
+ * take a second pass over their Q tiles.
  */
 int nvfp4_prefill_plan(const int32_t* qo_indptr_host, const int32_t* kv_lens_host,
                        const int32_t* kv_indptr_host, int32_t batch, int32_t num_q_heads,
                        int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
-                       int64_t l2_bytes, int32_t split_len, int32_t tile_waves,
-                       nvfp4kv_prefill_plan* plan);
+                       int64_t l2_bytes, int32_t cu_count, int32_t split_len,
+                       int32_t tile_waves, nvfp4kv_prefill_plan* plan);
 
 /*
  * paged_prefill_causal -- batched causal prefill attention over the NVFP4
- * paged cache ([PR #4769]: each KV tile is dequantized once into a bf16 LDS
- * staging tile outside the matrix-core loop; [PR #3575]: O(1) tile decode for
- * uniform batches, heaviest-first Q tiles, L2-gated order).
+ * paged cache ([PR #4769]: each KV tile is dequantized once into a 16-bit LDS
+ * staging tile outside the matrix-core loop -- f16 by default, since every
+ * E2M1 x E4M3 product is exact in f16 and the queries enter the f16 matrix
+ * instructions after an exact power-of-two rescale per row; bf16 staging
+ * with bf16 matrix instructions is plan->dequant_mode 3; [PR #3575]: O(1)
+ * tile decode for uniform batches, heaviest-first Q tiles, L2-gated order).
  *   q          bf16 [total_q][num_q_heads][head_dim], contiguous, 16-byte aligned.
  *   qo_indptr  int32 [batch+1] (device copy of the plan's host array).
  *   kv_indptr  int32 [batch+1]: request r's pages are
@@ -196,14 +222,16 @@ int nvfp4_prefill_plan(const int32_t* qo_indptr_host, const int32_t* kv_lens_hos
  *   caches     host pointer to the cache descriptor (its pointers are device
  *              pointers); geometry must match the plan.
  *   out        bf16 [total_q][num_q_heads][head_dim].
- *   sm_scale   softmax scale applied to q.k.
+ *   sm_scale   softmax scale applied to q.k; must be positive and finite
+ *              (NVFP4KV_EINVAL otherwise).
  *   plan       host pointer, from nvfp4_prefill_plan for these lengths.
  *   workspace  device buffer of at least plan->workspace_bytes (may be NULL
- *              when that is 0), 256-byte aligned, ZERO-FILLED before its first
- *              use: it holds the device work list and, for split Q tiles, the
- *              chunks' partial results and arrival counters, which every call
- *              leaves at zero again.  Calls that share a workspace must not
- *              overlap.
+ *              when that is 0), 256-byte aligned, with no required contents:
+ *              it holds the device work list and, for split Q tiles, the
+ *              chunks' partial results and arrival counters, all of which
+ *              the call itself initialises (the counters are zeroed by the
+ *              work-list kernel that runs first).  Calls that share a
+ *              workspace must not overlap.
  * Split Q tiles (plan->split_len > 0, batches too small to fill the GPU): the
  * KV range of a heavy Q tile is cut into chunks computed by separate
  * workgroups; the last chunk to finish merges the others' partial

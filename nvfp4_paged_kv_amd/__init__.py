@@ -61,7 +61,8 @@ class PlanStruct(ctypes.Structure):
                 ("num_tiles", "kv_bytes", "l2_bytes", "workspace_bytes")] + \
                [("split_len", ctypes.c_int32), ("max_chunks", ctypes.c_int32),
                 ("num_items", ctypes.c_int64), ("num_split_tiles", ctypes.c_int64),
-                ("dequant_mode", ctypes.c_int32)]
+                ("dequant_mode", ctypes.c_int32), ("cu_count", ctypes.c_int32),
+                ("schedule", ctypes.c_int32)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -92,7 +93,7 @@ def lib():
         P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         L.nvfp4_append_paged_kv.argtypes = [P, P, P, I64, P, P, P, P, P, P, I64, I32, I32, I32, P, P]
         L.nvfp4_append_paged_kv.restype = ctypes.c_int
-        L.nvfp4_prefill_plan.argtypes = [P, P, P, I32, I32, I32, I32, I32, I64, I32, I32,
+        L.nvfp4_prefill_plan.argtypes = [P, P, P, I32, I32, I32, I32, I32, I64, I32, I32, I32,
                                          ctypes.POINTER(PlanStruct)]
         L.nvfp4_prefill_plan.restype = ctypes.c_int
         L.paged_prefill_causal.argtypes = [P, P, P, P, P, ctypes.POINTER(Cache), P, ctypes.c_float,
@@ -128,6 +129,8 @@ _err_words: dict = {}
 
 
 def _norm_device(device) -> torch.device:
+    """torch.device with the current GPU's index filled in, so that "cuda" and
+    "cuda:N" name one workspace or error word."""
     device = torch.device(device)
     if device.type == "cuda" and device.index is None:
         device = torch.device("cuda", torch.cuda.current_device())
@@ -153,10 +156,13 @@ def read_device_error(device=None, clear: bool = True, word: Optional[torch.Tens
 
 
 def _scale_tensor(name: str, value, device: torch.device) -> torch.Tensor:
-    """Global decode scale as a device fp32 scalar, following the FlashInfer
-    PR #6204 page's scale contract: a float or CPU tensor is checked on the host
-    (ValueError); a device tensor is left to the kernel's own check, because
-    reading it here would synchronize the host with the stream."""
+    """The global decode scale as an fp32 scalar on `device` (scale contract of
+    the FlashInfer PR #6204 page, sections "code analysis" and "change in
+    error handling").  A Python number or a CPU tensor is already on the host,
+    so it is validated here and rejected with ValueError.  A GPU tensor is
+    passed through unread: only its shape, dtype, device and layout are
+    checked, and its value is validated by the kernels (a host read would
+    wait for the stream)."""
     if isinstance(value, torch.Tensor) and value.device.type == "cuda":
         if value.numel() != 1 or value.dtype != torch.float32:
             raise ValueError(f"{name} must be a scalar torch.float32 tensor")
@@ -171,7 +177,8 @@ def _scale_tensor(name: str, value, device: torch.device) -> torch.Tensor:
         value = float(value.reshape(()).item())
     value = float(value)
     if not math.isfinite(value) or value <= 0.0:
-        raise ValueError(f"{name} must be a positive finite global decode scale")
+        raise ValueError(f"{name}: a global decode scale has to be finite and greater than zero "
+                         f"(got {value!r})")
     return torch.full((), value, dtype=torch.float32, device=device)
 
 
@@ -269,7 +276,7 @@ class Plan:
 
     def __init__(self, qo_indptr, kv_lens, num_q_heads, num_kv_heads, head_dim, page_size,
                  kv_indptr=None, l2_bytes: int = 0, split_len: int = 0, tile_waves: int = 0,
-                 dequant_mode: int = 0):
+                 dequant_mode: int = 0, cu_count: int = 0, schedule: int = 0):
         qo = _host_int32(qo_indptr, "qo_indptr")
         kvl = _host_int32(kv_lens, "kv_lens")
         kvp = _host_int32(kv_indptr, "kv_indptr") if kv_indptr is not None else None
@@ -278,10 +285,12 @@ class Plan:
         self.struct = PlanStruct()
         _check(lib().nvfp4_prefill_plan(
             _ptr(qo), _ptr(kvl), _ptr(kvp), kvl.numel(), num_q_heads, num_kv_heads, head_dim,
-            page_size, l2_bytes, split_len, tile_waves, ctypes.byref(self.struct)),
+            page_size, l2_bytes, cu_count, split_len, tile_waves, ctypes.byref(self.struct)),
             "nvfp4_prefill_plan")
         self.struct.dequant_mode = int(dequant_mode)
-        self.qo_host, self.kv_lens_host = qo, kvl
+        if schedule:
+            self.struct.schedule = int(schedule)
+        self.qo_host, self.kv_lens_host, self.kv_indptr_host = qo, kvl, kvp
         self._workspace = {}
 
     def __getattr__(self, name):
@@ -295,18 +304,10 @@ class Plan:
             return None
         device = _norm_device(device)
         if device not in self._workspace:
-            # zero-filled once (a fill kernel); the kernels leave it zeroed
-            self._workspace[device] = torch.zeros(n, dtype=torch.uint8, device=device)
+            # no initial contents needed: each call writes its work list and
+            # zeroes its split counters before the prefill kernel reads them
+            self._workspace[device] = torch.empty(n, dtype=torch.uint8, device=device)
         return self._workspace[device]
-
-
-def _norm_device(device) -> torch.device:
-    """torch.device with the current GPU's index filled in, so that "cuda" and
-    "cuda:N" name one workspace."""
-    device = torch.device(device)
-    if device.type == "cuda" and device.index is None:
-        device = torch.device("cuda", torch.cuda.current_device())
-    return device
 
 
 def _host_int32(t, name) -> torch.Tensor:
@@ -320,16 +321,23 @@ def _host_int32(t, name) -> torch.Tensor:
     return t.to(torch.int32).contiguous()
 
 
+SCHEDULE_HEAVIEST, SCHEDULE_STREAM, SCHEDULE_REQUEST = 1, 2, 3
+
+
 def plan(qo_indptr, kv_lens, num_q_heads, num_kv_heads, head_dim, page_size, kv_indptr=None,
-         l2_bytes: int = 0, split_len: int = 0, tile_waves: int = 0, dequant_mode: int = 0) -> Plan:
-    """Host plan of one prefill batch.  split_len: KV tiles per chunk of a split
-    Q tile (0 automatic, > 0 forced, < 0 never); tile_waves: waves of 32 query
-    rows per workgroup (0 automatic, 4 or 8); dequant_mode: the dequant-placement
-    ablation (0: tiles decoded once into f16 LDS, the default; 1: K decoded in
-    registers inside the matrix loop; 2: byte-table decode; 3: bf16 staging and
-    bf16 matrix instructions)."""
+         l2_bytes: int = 0, split_len: int = 0, tile_waves: int = 0, dequant_mode: int = 0,
+         cu_count: int = 0, schedule: int = 0) -> Plan:
+    """Host plan of one prefill batch.  l2_bytes / cu_count: device L2 and CU
+    count to plan for (0: the current device's); split_len: KV tiles per chunk
+    of a split Q tile (0 automatic, > 0 forced, < 0 never); tile_waves: waves
+    of 32 query rows per workgroup (0 automatic, 4 or 8); dequant_mode: the
+    dequant-placement ablation (0: tiles decoded once into f16 LDS, the
+    default; 1: K decoded in registers inside the matrix loop; 2: byte-table
+    decode; 3: bf16 staging and bf16 matrix instructions); schedule: issue
+    order of the Q tiles (0: the plan's choice; SCHEDULE_HEAVIEST,
+    SCHEDULE_STREAM or SCHEDULE_REQUEST)."""
     return Plan(qo_indptr, kv_lens, num_q_heads, num_kv_heads, head_dim, page_size, kv_indptr,
-                l2_bytes, split_len, tile_waves, dequant_mode)
+                l2_bytes, split_len, tile_waves, dequant_mode, cu_count, schedule)
 
 
 def paged_prefill_causal(q: torch.Tensor, qo_indptr: torch.Tensor, kv_indptr: torch.Tensor,
@@ -358,6 +366,7 @@ def paged_prefill_causal(q: torch.Tensor, qo_indptr: torch.Tensor, kv_indptr: to
         raise ValueError("q/out must be [total_q, num_q_heads, head_dim]")
     if q.shape[0] != plan.total_q or q.shape[1] != plan.num_q_heads:
         raise ValueError("q does not match the plan")
+    _check_batch_arrays(plan, qo_indptr, kv_indptr, kv_lens, page_table)
     ws = plan.workspace(dev)
     err = dev_error if dev_error is not None else device_error_word(dev)
     cs = caches._struct()
@@ -416,6 +425,7 @@ def paged_decode(q: torch.Tensor, kv_indptr: torch.Tensor, page_table: torch.Ten
         raise ValueError("q/out must be [batch, num_q_heads, head_dim]")
     if q.shape[0] != plan.batch or q.shape[1] != plan.num_q_heads:
         raise ValueError("q does not match the plan")
+    _check_batch_arrays(plan, None, kv_indptr, kv_lens, page_table)
     ws = plan.workspace(dev)
     err = dev_error if dev_error is not None else device_error_word(dev)
     cs = caches._struct()
@@ -424,6 +434,28 @@ def paged_decode(q: torch.Tensor, kv_indptr: torch.Tensor, page_table: torch.Ten
         float(sm_scale), ctypes.byref(plan.struct), _ptr(ws), 0 if ws is None else ws.numel(),
         _ptr(err), _stream(dev)), "paged_decode")
     return out
+
+
+def _check_batch_arrays(plan, qo_indptr, kv_indptr, kv_lens, page_table):
+    """Element counts of the per-request device arrays against the plan (no
+    device read): the kernels index them by request and page without bounds."""
+    B = plan.batch
+    if qo_indptr is not None and qo_indptr.numel() != B + 1:
+        raise ValueError(f"qo_indptr must have batch + 1 = {B + 1} entries")
+    if kv_indptr.numel() != B + 1:
+        raise ValueError(f"kv_indptr must have batch + 1 = {B + 1} entries")
+    if kv_lens.numel() != B:
+        raise ValueError(f"kv_lens must have batch = {B} entries")
+    kvp = getattr(plan, "kv_indptr_host", None)
+    need = int(kvp[-1]) if kvp is not None and kvp.numel() == B + 1 else None
+    if need is None:
+        # pages each request needs, from the plan's host lengths
+        kvl = plan.kv_lens_host
+        ps = plan.page_size
+        need = int(((kvl.to(torch.int64) + ps - 1) // ps).sum()) if kvl.numel() else 0
+    if page_table.numel() < need:
+        raise ValueError(f"page_table has {page_table.numel()} entries; the batch's requests "
+                         f"own {need}")
 
 
 def _need_host(name):

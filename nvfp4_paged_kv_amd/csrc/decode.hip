@@ -418,7 +418,7 @@ extern "C" int paged_decode(const void* q, const int32_t* kv_indptr, const int32
                             const int32_t* kv_lens, const nvfp4kv_cache* caches, void* out,
                             float sm_scale, const nvfp4kv_decode_plan* plan, void* workspace,
                             int64_t workspace_bytes, uint32_t* dev_error, void* stream) {
-  if (!plan || !caches) return NVFP4KV_EINVAL;
+  if (!plan || !caches || !(sm_scale > 0.0f) || !(sm_scale <= 3.402823466e38f)) return NVFP4KV_EINVAL;
   const nvfp4kv_decode_plan& p = *plan;
   const nvfp4kv_cache& c = *caches;
   if (p.num_kv_heads != c.num_kv_heads || p.head_dim != c.head_dim || p.page_size != c.page_size ||

@@ -43,10 +43,12 @@ using namespace nvfp4kv;
 extern "C" int nvfp4_prefill_plan(const int32_t* qo_indptr_host, const int32_t* kv_lens_host,
                                   const int32_t* kv_indptr_host, int32_t batch,
                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                  int32_t page_size, int64_t l2_bytes, int32_t split_len,
-                                  int32_t tile_waves, nvfp4kv_prefill_plan* plan) {
+                                  int32_t page_size, int64_t l2_bytes, int32_t cu_count,
+                                  int32_t split_len, int32_t tile_waves,
+                                  nvfp4kv_prefill_plan* plan) {
   if (!plan || batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || page_size <= 0 ||
-      head_dim <= 0 || (batch > 0 && (!qo_indptr_host || !kv_lens_host)))
+      head_dim <= 0 || l2_bytes < 0 || cu_count < 0 ||
+      (batch > 0 && (!qo_indptr_host || !kv_lens_host)))
     return NVFP4KV_EINVAL;
   if (!(tile_waves == 0 || tile_waves == 4 || (tile_waves == 8 && head_dim == 128)))
     return NVFP4KV_EINVAL;
@@ -62,7 +64,10 @@ extern "C" int nvfp4_prefill_plan(const int32_t* qo_indptr_host, const int32_t* 
   p.num_kv_heads = num_kv_heads;
   p.head_dim = head_dim;
   p.page_size = page_size;
-  const int cu_count = l2_bytes > 0 ? 256 : device_props().cu_count;
+  // CUs the tile-width and split decisions size the batch against (0 = those
+  // of the current device)
+  const int cus = cu_count > 0 ? cu_count : device_props().cu_count;
+  p.cu_count = cus;
   p.block_n = kBlockN;
   // One pass of reductions over the host arrays ([PR #5043]: max lengths from
   // a vectorised reduction, not a per-request Python loop).
@@ -101,7 +106,7 @@ extern "C" int nvfp4_prefill_plan(const int32_t* qo_indptr_host, const int32_t* 
   // per CU.
   const bool wide = tile_waves == 8 ||
                     (tile_waves == 0 && head_dim == 128 &&
-                     qtiles8 * num_kv_heads >= (int64_t)kWideTilesPerCu * cu_count);
+                     qtiles8 * num_kv_heads >= (int64_t)kWideTilesPerCu * cus);
   p.block_q = wide ? bq8 : bq4;
   p.q_tiles_per_head = (max_q + p.block_q - 1) / p.block_q;
   p.max_tile_cost = max_cost;
@@ -111,7 +116,7 @@ extern "C" int nvfp4_prefill_plan(const int32_t* qo_indptr_host, const int32_t* 
   // 4-wave workgroups per CU) split the KV range of their heaviest Q tiles so
   // that every slot gets about the same number of KV tiles: chunk length =
   // total KV tiles / slots.
-  const int64_t slots = (int64_t)cu_count * (wide ? 1 : 2);
+  const int64_t slots = (int64_t)cus * (wide ? 1 : 2);
   p.num_items = p.num_tiles;
   if (split_len >= 0 && (split_len > 0 || p.num_tiles < slots)) {
     int64_t total_cost = 0;
@@ -149,13 +154,17 @@ extern "C" int nvfp4_prefill_plan(const int32_t* qo_indptr_host, const int32_t* 
   p.kv_bytes = tot_kv * num_kv_heads * (int64_t)(head_dim / 2 + head_dim / 16) * 2;
   if (l2_bytes > 0) {
     p.l2_bytes = l2_bytes;
-    p.num_xcd = 8;
+    p.num_xcd = cus >= 32 ? cus / 32 : 1;  // gfx950: 32 CUs per XCD
   } else {
     const DeviceProps& d = device_props();
     p.l2_bytes = d.l2_bytes_per_xcd * d.num_xcd;
     p.num_xcd = d.num_xcd;
   }
   p.head_first = 2 * p.kv_bytes <= p.l2_bytes;
+  // Issue order: heaviest first over everything when the KV fits in L2;
+  // otherwise stream order (each stream's KV fetched once into one XCD's L2)
+  // where it is available, else heaviest first.
+  p.schedule = !p.head_first && stream_order_available(p) ? kOrderStream : kOrderHeaviest;
   // Ragged or split batches need a device work list (and, when split, the
   // chunks' partials and arrival counters).
   p.workspace_bytes = workspace_layout(p).total;
@@ -235,4 +244,4 @@ extern "C" const char* nvfp4kv_status_string(int status) {
   }
 }
 
-extern "C" int nvfp4kv_abi_version(void) { return 101; }
+extern "C" int nvfp4kv_abi_version(void) { return 102; }

@@ -28,6 +28,21 @@ constexpr int kWideTilesPerCu = 4;
 constexpr int kMinSplit = 8;
 constexpr int kMaxChunks = 16;
 
+// Issue orders of the prefill's Q tiles (nvfp4kv_prefill_plan.schedule).
+// Stream order on ragged batches keeps each KV head's streams on one of the
+// kXcds XCDs (needs num_kv_heads % kXcds == 0) and ranks at most
+// kStreamOrderMaxReq requests in one workgroup's LDS.
+constexpr int kOrderHeaviest = 1;
+constexpr int kOrderStream = 2;
+constexpr int kOrderRequest = 3;
+constexpr int kXcds = 8;
+constexpr int kStreamOrderMaxReq = 8192;
+inline bool stream_order_available(const nvfp4kv_prefill_plan& p) {
+  const bool list = !p.uniform_q || p.split_len > 0;
+  return p.split_len == 0 &&
+         (!list || (p.num_kv_heads % kXcds == 0 && p.batch <= kStreamOrderMaxReq));
+}
+
 // Workspace layout of one prefill call (shared by the plan and the launcher):
 // [work list: 16 B per item][arrival counters: 2 x int32 per split tile]
 // [partials: per split tile, max_chunks x (rows x head_dim fp32 + 2 x rows fp32)].

@@ -71,7 +71,7 @@ struct PrefillArgs {
   FastDiv ps_div;
   int Hq, Hk;
   float sm_scale_log2;  // sm_scale * log2(e)
-  int B, QT, head_first, nxcd;
+  int B, QT, order, nxcd;  // order: kOrderHeaviest, kOrderStream or kOrderRequest
   int snake;  // every tile is resident at once: pair heavy with light tiles
   uint32_t num_tiles, num_items;
 };
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   } else {
     const uint32_t bh_n = (uint32_t)a.B * a.Hk;
     uint32_t bh, qrev;
-    if (a.head_first) {
+    if (a.order == kOrderHeaviest) {
       // heaviest Q tiles of every (request, head) first
       qrev = tile / bh_n;
       bh = tile - qrev * bh_n;
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
       // so that every CU gets one heavy and one light tile.
       const uint32_t half = (a.QT + 1) / 2;
       if (a.snake && qrev >= half) qrev = a.QT - 1 - (qrev - half);
-    } else {
+    } else if (a.order == kOrderStream) {
       // stream-major: XCD x (blockIdx % nxcd) owns a contiguous range of
       // (request, head) streams, each walked heaviest tile first
       const uint32_t nx = a.nxcd, x = tile % nx, s = tile / nx;
@@ -440,6 +440,11 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
       const uint32_t L = x * per + (x < rem ? x : rem) + s;
       bh = L / a.QT;
       qrev = L - bh * a.QT;
+    } else {
+      // request order: (request, head) streams in order, each one's Q tiles
+      // lightest first -- no reordering at all
+      bh = tile / a.QT;
+      qrev = a.QT - 1 - (tile - bh * a.QT);
     }
     b = bh / a.Hk;
     hk = bh - b * a.Hk;
@@ -764,10 +769,6 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) o[db] = acc[db];
     l_tot = l_acc;
-    if (tid == 0) {  // leave the counters zeroed for the next call
-      __hip_atomic_store(arrive, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(arrive + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
   }
 
   // ---- epilogue: O / l * g_v -> bf16; lane holds O^T[d][row n]
@@ -828,8 +829,6 @@ __device__ __forceinline__ int block_exclusive_scan(int sum, int* warp_tot) {
 // stream's KV tiles are fetched once into that XCD's L2 and reused by its Q
 // tiles while they are resident.  Needs Hk % 8 == 0 (every XCD then gets the
 // same number of items) and B <= kStreamOrderMaxReq.
-constexpr int kStreamOrderMaxReq = 8192;
-constexpr int kXcds = 8;
 
 __device__ void worklist_stream_order(const int32_t* __restrict__ qo, const int32_t* __restrict__ kvl,
                                       int B, int Hk, int BQ, int QT, int4* __restrict__ list,
@@ -897,19 +896,63 @@ __device__ void worklist_stream_order(const int32_t* __restrict__ qo, const int3
   }
 }
 
+// Request order: items in (request, Q tile ascending, chunk, KV head) order,
+// the positions from a scan of the item counts over the (request, Q tile)
+// pairs.
+__device__ void worklist_request_order(const int32_t* __restrict__ qo, const int32_t* __restrict__ kvl,
+                                       int B, int Hk, int BQ, int QT, int split_len,
+                                       int4* __restrict__ list, int* n_split, int* warp_tot) {
+  const int tid = threadIdx.x;
+  const int64_t n = (int64_t)B * QT, per = (n + 1023) / 1024;
+  const int64_t i0 = min(n, tid * per), i1 = min(n, i0 + per);
+  auto chunks_of = [&](int64_t i, int& rq, int& t, int& lq, int& off, int& c) {
+    rq = (int)(i / QT);
+    t = (int)(i - (int64_t)rq * QT);
+    lq = qo[rq + 1] - qo[rq];
+    off = kvl[rq] - lq;
+    if (t * BQ >= lq) return 0;
+    c = tile_cost(lq, off, t, BQ);
+    return split_len > 0 ? (c + split_len - 1) / split_len : 1;
+  };
+  int cnt = 0, rq, t, lq, off, c;
+  for (int64_t i = i0; i < i1; ++i) cnt += chunks_of(i, rq, t, lq, off, c);
+  int pos = block_exclusive_scan(cnt, warp_tot);
+  for (int64_t i = i0; i < i1; ++i) {
+    const int nch = chunks_of(i, rq, t, lq, off, c);
+    if (nch == 0) continue;
+    const int sid = nch > 1 ? atomicAdd(n_split, Hk) : -1;
+    for (int k = 0; k < nch; ++k, ++pos) {
+      const int beg = k * c / nch, end = (k + 1) * c / nch;
+      for (int h = 0; h < Hk; ++h)
+        list[(int64_t)pos * Hk + h] = make_int4(rq, t * Hk + h, (beg << 16) | end,
+                                                nch > 1 ? ((sid + h) << 10) | (k << 5) | nch : -1);
+    }
+  }
+}
+
+// The work list of one call, in the given issue order.  It also zeroes the
+// split tiles' arrival counters, so that every call starts from zero whatever
+// an earlier call (or the workspace's first contents) left there.
 __global__ __launch_bounds__(1024) void worklist_kernel(const int32_t* __restrict__ qo,
                                                         const int32_t* __restrict__ kvl, int B,
                                                         int Hk, int BQ, int QT, int split_len,
-                                                        int stream_order, int4* __restrict__ list) {
+                                                        int order, int4* __restrict__ list,
+                                                        int* __restrict__ counters,
+                                                        int64_t num_counters) {
   __shared__ int hist[kCostBuckets];
   __shared__ int warp_tot[16];
   __shared__ int n_split;
   const int tid = threadIdx.x;
+  for (int64_t i = tid; i < num_counters; i += 1024) counters[i] = 0;
   for (int i = tid; i < kCostBuckets; i += 1024) hist[i] = 0;
   if (tid == 0) n_split = 0;
   __syncthreads();
-  if (stream_order) {
+  if (order == kOrderStream) {
     worklist_stream_order(qo, kvl, B, Hk, BQ, QT, list, hist, warp_tot);
+    return;
+  }
+  if (order == kOrderRequest) {
+    worklist_request_order(qo, kvl, B, Hk, BQ, QT, split_len, list, &n_split, warp_tot);
     return;
   }
   for (int64_t i = tid; i < (int64_t)B * QT; i += 1024) {
@@ -990,7 +1033,7 @@ extern "C" int paged_prefill_causal(const void* q, const int32_t* qo_indptr,
                                     float sm_scale, const nvfp4kv_prefill_plan* plan,
                                     void* workspace, int64_t workspace_bytes, uint32_t* dev_error,
                                     void* stream) {
-  if (!plan || !caches) return NVFP4KV_EINVAL;
+  if (!plan || !caches || !(sm_scale > 0.0f) || !(sm_scale <= 3.402823466e38f)) return NVFP4KV_EINVAL;
   const nvfp4kv_prefill_plan& p = *plan;
   const nvfp4kv_cache& c = *caches;
   if (p.num_kv_heads != c.num_kv_heads || p.head_dim != c.head_dim ||
@@ -1029,27 +1072,26 @@ extern "C" int paged_prefill_causal(const void* q, const int32_t* qo_indptr,
   a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
   a.B = p.batch;
   a.QT = p.q_tiles_per_head;
-  a.head_first = p.head_first;
+  if (p.schedule == kOrderStream ? !stream_order_available(p)
+                                 : p.schedule != kOrderHeaviest && p.schedule != kOrderRequest)
+    return NVFP4KV_EUNSUPPORTED;
+  a.order = p.schedule;
   a.nxcd = p.num_xcd > 0 ? p.num_xcd : 1;
   a.num_tiles = (uint32_t)p.num_tiles;
   a.num_items = (uint32_t)p.num_items;
   const WorkspaceLayout wl = workspace_layout(p);
   // the heavy/light pairing assumes two co-resident workgroups per CU
   a.snake = p.block_q * (p.num_q_heads / p.num_kv_heads) == 128 &&
-            p.num_tiles <= 2 * (int64_t)device_props().cu_count;
+            p.num_tiles <= 2 * (int64_t)p.cu_count;
   if (!p.uniform_q || p.split_len > 0) {
     a.worklist = (const int4*)workspace;
     a.counters = (int*)((uint8_t*)workspace + wl.counters);
     a.partials = (float*)((uint8_t*)workspace + wl.partials);
     a.partial_floats = wl.partial_bytes / 4;
     a.max_chunks = p.max_chunks;
-    // stream order when the KV working set does not fit in L2 and nothing is
-    // split (otherwise: every item heaviest first)
-    const int stream_order = !p.head_first && p.split_len == 0 && p.num_kv_heads % kXcds == 0 &&
-                             p.batch <= kStreamOrderMaxReq;
     hipLaunchKernelGGL(worklist_kernel, dim3(1), dim3(1024), 0, s, qo_indptr, kv_lens, p.batch,
-                       p.num_kv_heads, p.block_q, p.q_tiles_per_head, p.split_len, stream_order,
-                       (int4*)workspace);
+                       p.num_kv_heads, p.block_q, p.q_tiles_per_head, p.split_len, p.schedule,
+                       (int4*)workspace, a.counters, 2 * p.num_split_tiles);
   }
   const int G = p.num_q_heads / p.num_kv_heads;
   const int D = p.head_dim;

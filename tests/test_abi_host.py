@@ -33,12 +33,13 @@ def test_library_exports_every_declared_symbol(K):
     L = ctypes.CDLL(K.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert K.lib().nvfp4kv_abi_version() == 101
+    assert K.lib().nvfp4kv_abi_version() == 102
     assert K.lib().nvfp4kv_status_string(-3).startswith(b"inconsistent")
 
 
-def _plan(K, qo, kv, hq=32, hk=8, d=128, ps=16, **kw):
-    return K.plan(torch.as_tensor(qo), torch.as_tensor(kv), hq, hk, d, ps, l2_bytes=32 << 20, **kw)
+def _plan(K, qo, kv, hq=32, hk=8, d=128, ps=16, cu_count=256, **kw):
+    return K.plan(torch.as_tensor(qo), torch.as_tensor(kv), hq, hk, d, ps, l2_bytes=32 << 20,
+                  cu_count=cu_count, **kw)
 
 
 def test_plan_split_workspace_layout(K):
@@ -86,7 +87,7 @@ def test_plan_max_lens(K, dtype, batch, page_size):
     kvp = torch.zeros(batch + 1, dtype=torch.int64)
     kvp[1:] = torch.cumsum(npg, 0)
     p = K.plan(qo.to(torch.int32), kv.to(dtype), 32, 8, 128, page_size, kv_indptr=kvp.to(torch.int32),
-               l2_bytes=32 << 20)
+               l2_bytes=32 << 20, cu_count=256)
     assert p.max_q_len == int((qo[1:] - qo[:-1]).max())
     assert p.max_kv_len == int(kv.max())
     assert p.total_q == int(q.sum()) and p.total_kv == int(kv.sum())
@@ -101,6 +102,11 @@ def test_plan_max_lens(K, dtype, batch, page_size):
     assert p.kv_bytes == int(kv.sum()) * 8 * (64 + 8) * 2
     assert p.head_first == int(2 * p.kv_bytes <= (32 << 20))
     assert (p.workspace_bytes == 0) == (bool(p.uniform_q) and p.split_len == 0)
+    # issue order: heaviest first when the KV fits in L2, else stream order
+    # where it is available (no split; 8 KV heads; at most 8192 requests)
+    assert p.schedule == (K.SCHEDULE_HEAVIEST if p.head_first or p.split_len > 0
+                          else K.SCHEDULE_STREAM)
+    assert p.cu_count == 256
 
 
 def test_plan_uniform_flags_and_tiles(K):
@@ -260,3 +266,67 @@ def test_plan_bench_paths_agree(K):
     import bench
     res = bench.bench_plan(K, torch, np, batches=(64,), reps=2)
     assert set(res["64"]) == {"native_us", "python_loop_us", "torch_vectorised_us"}
+
+
+def test_plan_cu_count_is_an_explicit_input(K):
+    """The CU count the plan sizes tiles and splits for is its own argument,
+    independent of the L2 capacity given to the gate: 512 4-wave tiles fill
+    the 2 x 256 slots of 256 CUs (no split) but not the 2 x 304 of 304 CUs
+    (their heavy tiles are split); the L2 size alone changes neither."""
+    p = _plan(K, [0, 2048], [2048], cu_count=256)
+    assert p.cu_count == 256 and p.split_len == 0 and p.num_xcd == 8
+    q = _plan(K, [0, 2048], [2048], cu_count=304)
+    assert q.cu_count == 304 and q.split_len > 0 and q.num_xcd == 9
+    expect = _expected_split([2048], [2048], 8, 32, 2 * 304)
+    assert (q.split_len, q.max_chunks, q.num_items, q.num_split_tiles) == expect
+    r = K.plan(torch.tensor([0, 2048]), torch.tensor([2048]), 32, 8, 128, 16, l2_bytes=1 << 40,
+               cu_count=256)
+    assert (r.split_len, r.num_items, r.head_first) == (0, p.num_items, 1)
+    with pytest.raises(ValueError):
+        K.plan(torch.tensor([0, 16]), torch.tensor([16]), 32, 8, 128, 16, cu_count=-1)
+    with pytest.raises(ValueError):
+        K.plan(torch.tensor([0, 16]), torch.tensor([16]), 32, 8, 128, 16, l2_bytes=-5)
+
+
+def test_plan_schedule_override(K):
+    """A caller-chosen issue order is kept in the plan as given."""
+    p = _plan(K, [0, 2048], [2048], schedule=K.SCHEDULE_REQUEST)
+    assert p.schedule == K.SCHEDULE_REQUEST
+    p = _plan(K, [0, 2048], [2048])
+    assert p.schedule == K.SCHEDULE_HEAVIEST and p.head_first == 1
+
+
+def test_attention_entry_points_reject_bad_sm_scale(K):
+    """sm_scale must be positive and finite: checked by the C entry points
+    before anything is read or enqueued (null buffers are never touched)."""
+    p = _plan(K, [0, 64], [64])
+    L = K.lib()
+    for bad in (0.0, -0.125, float("nan"), float("inf")):
+        st = L.paged_prefill_causal(None, None, None, None, None, ctypes.byref(K.Cache()), None, bad,
+                                    ctypes.byref(p.struct), None, 0, None, None)
+        assert st == K.EINVAL, bad
+        d = K.decode_plan(torch.tensor([64], dtype=torch.int32), 32, 8, 128, 16)
+        st = L.paged_decode(None, None, None, None, ctypes.byref(K.Cache()), None, bad,
+                            ctypes.byref(d.struct), None, 0, None, None)
+        assert st == K.EINVAL, bad
+
+
+def test_binding_checks_batch_array_sizes(K):
+    """The binding compares the per-request arrays with the plan before any
+    launch (host-side sizes only): qo_indptr and kv_indptr need batch + 1
+    entries, kv_lens batch, the page table at least the pages the requests
+    own."""
+    qo, kv = torch.tensor([0, 16, 48], dtype=torch.int32), torch.tensor([40, 32], dtype=torch.int32)
+    kvp = torch.tensor([0, 3, 5], dtype=torch.int32)
+    p = K.plan(qo, kv, 8, 2, 64, 16, kv_indptr=kvp)
+    q = torch.zeros((48, 8, 64), dtype=torch.bfloat16)
+    out = torch.empty_like(q)
+    pt = torch.arange(5, dtype=torch.int32)
+    cache = K.PagedCache(*(torch.zeros(1, dtype=torch.uint8) for _ in range(4)),
+                         torch.ones(()), torch.ones(()))
+    cases = [(qo[:2], kvp, kv, pt, "qo_indptr"), (qo, kvp[:2], kv, pt, "kv_indptr"),
+             (qo, kvp, kv[:1], pt, "kv_lens"), (qo, kvp, kv, pt[:4], "page_table")]
+    for a, b, c, d, name in cases:
+        with pytest.raises(ValueError, match=name):
+            K._check_batch_arrays(p, a, b, c, d)
+    K._check_batch_arrays(p, qo, kvp, kv, pt)

@@ -142,7 +142,7 @@ def test_host_scale_raises_value_error(K):
     w = W.tiny("cuda")
     cache = K.PagedCache.empty(w.num_pages, w.page_size, 2, 64, "cuda")
     for bad in (0.0, -1.0, float("nan"), float("inf"), torch.tensor(-2.0)):
-        with pytest.raises(ValueError, match="positive finite global decode scale"):
+        with pytest.raises(ValueError, match="finite and greater than zero"):
             K.nvfp4_append_paged_kv(w.k, w.v, w.slot_mapping, bad, 1.0, cache.k_cache, cache.v_cache,
                                     cache.k_sf, cache.v_sf, w.page_size)
 

@@ -147,27 +147,34 @@ def test_prefill_ragged_chunked_sampled(K, oracle):
 
 
 def test_schedule_orders_give_identical_bits(K):
-    """Uniform O(1) decode (head-first and stream-major) and the device work
-    list (heaviest item first, and stream order) compute every tile the same
-    way: outputs are bitwise identical."""
+    """Uniform O(1) decode and the device work list, each in the three issue
+    orders (heaviest first, stream order, request order), and split Q tiles
+    in heaviest-first and request order, compute every tile the same way:
+    outputs are bitwise identical."""
     banner("schedule order independence")
     w = W.make_attention("order", [256] * 6, [300] * 6, 32, 8, 128, 16, 200, seed=13, device="cuda",
                          scales="amax")
-    base, cache, plan = run_gpu(K, w, plan=K.plan(torch.from_numpy(w.qo_indptr),
-                                                   torch.from_numpy(w.kv_lens), 32, 8, 128, 16,
-                                                   split_len=-1))
-    outs = []
-    for hf, uq in [(1 - plan.head_first, 1), (1, 0), (0, 0)]:
-        p2 = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), 32, 8, 128, 16,
-                    split_len=-1)
-        p2.struct.head_first = hf
-        if not uq:
-            p2.struct.uniform_q = 0
-            p2.struct.workspace_bytes = ((p2.struct.num_items * 16 + 255) // 256) * 256
-        o, _, _ = run_gpu(K, w, cache=cache, plan=p2)
-        outs.append(o)
-    for o in outs:
-        assert torch.equal(o, base)
+
+    def mk(**kw):
+        return K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), 32, 8, 128, 16, **kw)
+
+    base, cache, plan = run_gpu(K, w, plan=mk(split_len=-1))
+    runs = 0
+    for uq in (1, 0):
+        for order in (K.SCHEDULE_HEAVIEST, K.SCHEDULE_STREAM, K.SCHEDULE_REQUEST):
+            p2 = mk(split_len=-1, schedule=order)
+            if not uq:
+                p2.struct.uniform_q = 0
+                p2.struct.workspace_bytes = ((p2.struct.num_items * 16 + 255) // 256) * 256
+            o, _, _ = run_gpu(K, w, cache=cache, plan=p2)
+            assert torch.equal(o, base), (uq, order)
+            runs += 1
+    split = [run_gpu(K, w, cache=cache, plan=mk(split_len=2, schedule=order))[0]
+             for order in (K.SCHEDULE_HEAVIEST, K.SCHEDULE_REQUEST)]
+    assert torch.equal(split[0], split[1])
+    with pytest.raises(K.NVFP4KVError, match="unsupported"):
+        run_gpu(K, w, cache=cache, plan=mk(split_len=2, schedule=K.SCHEDULE_STREAM))
+    assert runs == 6
 
 
 def test_stream_ordered_work_list_layout(K):
@@ -182,8 +189,7 @@ def test_stream_ordered_work_list_layout(K):
     w = W.make_attention("wl", q_lens, kv_lens, 32, 8, 128, 16, 800, seed=17, device="cuda",
                          scales="amax")
     plan = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), 32, 8, 128, 16,
-                  split_len=-1, tile_waves=8)
-    plan.struct.head_first = 0
+                  split_len=-1, tile_waves=8, schedule=K.SCHEDULE_STREAM)
     out, cache, plan = run_gpu(K, w, plan=plan)
     torch.cuda.synchronize()
     n = plan.num_items

@@ -343,3 +343,32 @@ def test_online_softmax_regrouping_matches_definition(oracle, block, slack, chun
             got = _flash_rows(q[rows, hq], Kr[:, hq // G], Vr[:, hq // G], w.sm_scale, nkeys, block,
                               slack, chunks)
             np.testing.assert_allclose(got, ref[rows, hq], rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_dequant_rows_vs_table_decode(oracle, D):
+    """oracle.dequant_rows (the helper the low-precision variant study builds
+    its references from) against decode_numpy, which decodes with the OCP E2M1
+    grid golden file and torch's float8_e4m3fn table: random code bytes
+    (every nibble), random finite scale bytes, rows in a shuffled order with
+    repeats, and a global scale that is not a power of two."""
+    rng = np.random.default_rng(D)
+    n_rows = 300
+    cache = rng.integers(0, 256, (n_rows, D // 2), dtype=np.uint8)
+    sf = rng.integers(0, 0x7F, (n_rows, D // 16), dtype=np.uint8)  # finite E4M3FN codes
+    rows = rng.integers(0, n_rows, 777).astype(np.int64)
+    g = 0.0173
+    got = oracle.dequant_rows(cache, sf, rows, D, g)
+    ref = decode_numpy(cache, sf, g)[rows]
+    assert got.shape == (rows.size, D)
+    assert np.array_equal(got, ref)
+    # a dropped nibble swap or a scale read from the neighbouring block would
+    # show up on these hand-built rows
+    c = np.zeros((1, D // 2), np.uint8)
+    c[0, 0] = 0x1F  # element 0: code 0xF (-6), element 1: code 0x1 (0.5)
+    s = np.full((1, D // 16), 0x38, np.uint8)  # 1.0
+    s[0, 1] = 0x40  # block 1: 2.0
+    c[0, 8] = 0x02  # element 16 (block 1): code 2 (1.0) -> 2.0
+    one = oracle.dequant_rows(c, s, np.zeros(1, np.int64), D, 1.0)[0]
+    assert one[0] == -6.0 and one[1] == 0.5 and one[16] == 2.0
+    assert np.count_nonzero(one) == 3
