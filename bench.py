@@ -10,11 +10,22 @@ reported separately.
 
 Prints one JSON line.  `value` is causal-prefill TFLOP/s over the whole step
 (algorithmic flops 4 * head_dim * allowed (query, key) pairs per query head,
-divided by the step time).  Also reported: per-kernel launch durations
-(HIP events on the launch stream around replays of a graph of back-to-back
-launches of that kernel), the roofline of the dominant kernel, the append's
-achieved GB/s on this workload and on the 65,536-token append stress
-workload, and the CPU oracle timed on a bounded sample.
+divided by the step time).  Also reported:
+  * roofline: the prefill kernel on that workload (the dominant kernel),
+    launch duration from HIP events on the launch stream around replays of a
+    graph of back-to-back launches, against the 0.40 target;
+  * configs: every workload (the 2x128 small batch, the 2048x2048 prefill,
+    the 1024x1024 uniform batch, the ragged chunked-prefill batch, the
+    65,536-token append) with its prefill TFLOP/s and append GB/s and their
+    fractions of the MI355X roofline;
+  * schedule: the prefill of the two large batches under the three issue
+    orders (heaviest first, stream order, request order);
+  * the decode step, the dequant-placement ablation, the measured achievable
+    peaks, the plan's host time, and the CPU oracle timed on bounded samples.
+
+Before the W warm-up steps the step runs untimed until the clocks have
+settled (at least SETTLE_MS of back-to-back steps; reported as settle_steps):
+the GPU needs ~30-40 ms of sustained work to leave its idle clocks.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -22,6 +33,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -30,7 +42,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "causal prefill TFLOP/s + append GB/s on NVFP4 paged KV (% of MI355X roofline)"
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
-BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 (= f16) MFMA, TFLOP/s
+PREFILL_TARGET_FRAC = 0.40  # of the MFMA peak, on the 2048x2048 prefill
+APPEND_TARGET_FRAC = 0.70   # of HBM bandwidth, on the 65,536-token append
+SETTLE_MS = 60.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -55,14 +70,24 @@ def append_bytes(tokens, heads, d):
     return tokens * heads * (2 * d + d // 2 + d // 16) * 2 + 8 * tokens
 
 
+def tflops_row(flops, ms):
+    t = flops / (ms * 1e-3) / 1e12
+    return {"avg_launch_us": round(ms * 1e3, 2), "TFLOP_s": round(t, 1), "frac": round(t / BF16_PEAK_TFLOPS, 4)}
+
+
+def gbs_row(nbytes, ms, key="avg_launch_us"):
+    g = nbytes / (ms * 1e-3) / 1e9
+    return {key: round(ms * 1e3, 2), "GB_s": round(g, 1), "frac": round(g / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
-    # the clocks settle after ~30-40 ms of sustained launches; 1000 warm-up
-    # steps (~60 ms) reach the steady state the timed steps measure
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload rows and the schedule comparison")
     ap.add_argument("--no-append-stress", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--no-achievable", action="store_true",
@@ -70,7 +95,7 @@ def main():
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the dequant-placement ablation of the prefill")
     ap.add_argument("--ablation-only", action="store_true",
-                    help="only launch the prefill under the three dequant placements (for counters)")
+                    help="only launch the prefill under the dequant placements (for counters)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (HBM-counter calibration)")
     args = ap.parse_args()
@@ -123,10 +148,18 @@ def main():
         cache.append(w.k, w.v, w.slot_mapping)
         K.paged_prefill_causal(w.q, qo_d, kvp_d, pt_d, kvl_d, cache, out, w.sm_scale, plan=plan)
 
+    # clock settling (untimed), then the W warm-up steps, then exactly K timed steps
+    settle = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < SETTLE_MS:
+        for _ in range(50):
+            step()
+        settle += 50
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # timed region: K steps, bracketed by device synchronization
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
@@ -151,6 +184,7 @@ def main():
     G = w.num_q_heads // w.num_kv_heads
     kernel_name = f"prefill_kernel<{w.head_dim},{G},{plan.block_q * G // 32},{'true' if 64 % w.page_size == 0 else 'false'},0>"
     traffic = _traffic("prefill_2k")
+    frac = pre_tflops / BF16_PEAK_TFLOPS
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -158,6 +192,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -167,27 +202,52 @@ def main():
         "config": {"workload": w.name, "batch": 1, "q_len": 2048, "kv_len": 2048,
                    "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128, "page_size": 16,
                    "kv_format": "nvfp4 (e2m1 + e4m3 per 16, fp32 global scale)",
+                   "staging": "f16 LDS tile, f16 MFMA (bf16 staging + bf16 MFMA: dequant_ablation "
+                              "lds_once_per_tile_bf16)",
                    "step": "append 2048 K/V rows + causal paged prefill",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": kernel_name,
                      "achieved": round(pre_tflops, 2), "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4),
+                     "unit": "TFLOP/s", "frac": round(frac, 4),
                      "traffic": traffic, "flops_per_launch": flops,
-                     "avg_launch_us": round(pre_ms * 1e3, 2)},
-        "append": {"bound": "hbm", "bytes_per_launch": abytes, "avg_launch_us": round(app_ms * 1e3, 2),
-                   "achieved_GBps": round(abytes / (app_ms * 1e-3) / 1e9, 1), "peak_GBps": HBM_PEAK_GBS,
-                   "frac": round(abytes / (app_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                     "avg_launch_us": round(pre_ms * 1e3, 2),
+                     "target_frac": PREFILL_TARGET_FRAC, "meets_target": bool(frac >= PREFILL_TARGET_FRAC)},
+        "append": {"bound": "hbm", "bytes_per_launch": abytes, **gbs_row(abytes, app_ms)},
         "plan_host_us": round(plan_us, 2),
         "plan_bench": bench_plan(K, torch, np),
         "kernel_source_hash": kernel_source_hash(),
     }
+    configs = {}
+    if not args.no_configs:
+        configs["small_2x128"] = bench_config_small(K, W, dev, torch)
+    configs["prefill_2k"] = {"workload": w.name, "prefill": {"flops_per_launch": flops, **tflops_row(flops, pre_ms)},
+                             "append": {"bytes_per_launch": abytes, **gbs_row(abytes, app_ms)}}
+    del cache, out
+    if not args.no_configs:
+        configs["uniform_1024x1024"], result["schedule_uniform_1024x1024"] = bench_config_large(
+            K, W.uniform_batch_1k(dev), torch)
+        torch.cuda.empty_cache()
+        configs["ragged_chunked_256"], result["schedule_ragged_chunked_256"] = bench_config_large(
+            K, W.ragged_chunked(dev), torch, chunk_append=True)
+        torch.cuda.empty_cache()
     if not args.no_append_stress:
-        result["append_stress"] = bench_append_stress(K, W, dev, torch, np)
+        st = bench_append_stress(K, W, dev, torch, np)
+        result["append_stress"] = st
+        configs["append_stress_65536"] = {"workload": st["workload"], "append": {
+            "bytes_per_launch": st["bytes_per_launch"], "cold_median_us": st["median_launch_us"],
+            "cold_back_to_back_us": st["back_to_back_avg_us"], "frac": st["frac"],
+            "frac_back_to_back": st["frac_back_to_back"]}}
+    result["configs"] = configs
     if not args.no_decode:
         result["decode"] = bench_decode(K, W, dev, torch, np)
     if not args.no_ablation:
-        result["dequant_ablation"] = bench_dequant_ablation(K, w, cache, (qo_d, kvp_d, pt_d, kvl_d), out,
-                                                            torch)
+        w2 = W.prefill_2k(dev)
+        c2 = K.PagedCache.empty(w2.num_pages, w2.page_size, w2.num_kv_heads, w2.head_dim, dev,
+                                w2.k_scale, w2.v_scale)
+        c2.append(w2.k, w2.v, w2.slot_mapping)
+        result["dequant_ablation"] = bench_dequant_ablation(K, w2, c2, (qo_d, kvp_d, pt_d, kvl_d),
+                                                            torch.empty_like(w2.q), torch)
+        del w2, c2
     if not args.no_achievable:
         ach = bench_achievable(W, dev, torch, np)
         ach["prefill_frac_of_mfma_loop"] = round(pre_tflops / ach["mfma_bf16_TFLOPs"], 4)
@@ -197,7 +257,7 @@ def main():
             ach["append_stress_frac_of_traffic_probe"] = round(got / ach["append_traffic_GBps"], 4)
         result["achievable"] = ach
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, flops)
+        result["cpu_baseline"] = cpu_baseline(w, flops, W, dev, torch, np)
     print(json.dumps(result), flush=True)
 
 
@@ -225,8 +285,83 @@ def graph_launch_ms(torch, fn, per_graph=50, replays=20):
     return e0.elapsed_time(e1) / (per_graph * replays)
 
 
+def _dev_arrays(w, dev, torch):
+    return [torch.from_numpy(x).to(dev) for x in (w.qo_indptr, w.kv_indptr, w.page_table, w.kv_lens)]
+
+
+def bench_config_small(K, W, dev, torch):
+    """The 2 x 128 small batch (head_dim 64, 4/2 heads): launch-latency bound."""
+    w = W.tiny(dev)
+    cache = K.PagedCache.empty(w.num_pages, w.page_size, w.num_kv_heads, w.head_dim, dev,
+                               w.k_scale, w.v_scale)
+    cache.append(w.k, w.v, w.slot_mapping)
+    args = _dev_arrays(w, dev, torch)
+    plan = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), w.num_q_heads,
+                  w.num_kv_heads, w.head_dim, w.page_size)
+    out = torch.empty_like(w.q)
+    pre = graph_launch_ms(torch, lambda: K.paged_prefill_causal(w.q, *args, cache, out, w.sm_scale, plan=plan))
+    app = graph_launch_ms(torch, lambda: cache.append(w.k, w.v, w.slot_mapping))
+    flops = attention_flops(w.q_lens, w.kv_lens, w.num_q_heads, w.head_dim)
+    nbytes = append_bytes(int(w.kv_lens.sum()), w.num_kv_heads, w.head_dim)
+    return {"workload": w.name, "prefill": {"flops_per_launch": flops, **tflops_row(flops, pre)},
+            "append": {"bytes_per_launch": nbytes, **gbs_row(nbytes, app)},
+            "note": "a few microseconds of work: bound by launch latency, not by the roofline"}
+
+
+def bench_config_large(K, w, torch, chunk_append=False):
+    """A large batch: the append of its new rows and the prefill under the
+    plan's own choices, then the prefill under each issue order (heaviest
+    first over every stream, stream order, request order; bitwise the same
+    results).  chunk_append: only the trailing q_len rows of each request
+    are the step's new rows (the prefix is appended once, untimed)."""
+    dev = w.q.device
+    cache = K.PagedCache.empty(w.num_pages, w.page_size, w.num_kv_heads, w.head_dim, dev,
+                               w.k_scale, w.v_scale)
+    cache.append(w.k, w.v, w.slot_mapping)
+    args = _dev_arrays(w, dev, torch)
+    out = torch.empty_like(w.q)
+    flops = attention_flops(w.q_lens, w.kv_lens, w.num_q_heads, w.head_dim)
+    if chunk_append:
+        import numpy as np
+        rows = np.concatenate([np.arange(w.kv_token_indptr[r + 1] - w.q_lens[r], w.kv_token_indptr[r + 1])
+                               for r in range(w.batch)])
+        ri = torch.from_numpy(rows).to(dev)
+        k, v, slots = w.k.index_select(0, ri), w.v.index_select(0, ri), w.slot_mapping.index_select(0, ri)
+    else:
+        k, v, slots = w.k, w.v, w.slot_mapping
+    app = graph_launch_ms(torch, lambda: cache.append(k, v, slots), per_graph=5, replays=4)
+    nbytes = append_bytes(k.shape[0], w.num_kv_heads, w.head_dim)
+
+    def mk(schedule=0):
+        return K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), w.num_q_heads,
+                      w.num_kv_heads, w.head_dim, w.page_size, schedule=schedule)
+
+    plan = mk()
+    pre = graph_launch_ms(torch, lambda: K.paged_prefill_causal(w.q, *args, cache, out, w.sm_scale, plan=plan),
+                          per_graph=4, replays=3)
+    row = {"workload": w.name, "prefill": {"flops_per_launch": flops, "schedule": plan.schedule,
+                                           "block_q": plan.block_q, "split_len": plan.split_len,
+                                           **tflops_row(flops, pre)},
+           "append": {"bytes_per_launch": nbytes, "rows": int(k.shape[0]), **gbs_row(nbytes, app)}}
+    sched = {}
+    for name, s in (("heaviest_first", K.SCHEDULE_HEAVIEST), ("stream_order", K.SCHEDULE_STREAM),
+                    ("request_order", K.SCHEDULE_REQUEST)):
+        p = mk(s)
+        ms = graph_launch_ms(torch, lambda: K.paged_prefill_causal(w.q, *args, cache, out, w.sm_scale, plan=p),
+                             per_graph=4, replays=3)
+        sched[name] = tflops_row(flops, ms)
+    base = sched["request_order"]["avg_launch_us"]
+    for name in ("heaviest_first", "stream_order"):
+        sched[name]["speedup_vs_request_order"] = round(base / sched[name]["avg_launch_us"], 3)
+    sched["plan_choice"] = {1: "heaviest_first", 2: "stream_order", 3: "request_order"}[plan.schedule]
+    bits = K.read_device_error(dev)
+    if bits:
+        raise SystemExit(f"device error bits {bits} on {w.name}")
+    return row, sched
+
+
 def bench_dequant_ablation(K, w, cache, dev_args, out, torch, per_graph=50, replays=20):
-    """The 2048x2048 prefill under the three dequant placements of the PR #4769
+    """The 2048x2048 prefill under the dequant placements of the PR #4769
     page's comparison (graph-timed launches; 4-wave tiles, as the plan picks):
     tiles decoded once per workgroup into f16 LDS (the kernel's own design), K
     decoded in registers inside the matrix loop, a byte-table decode, and the
@@ -240,9 +375,7 @@ def bench_dequant_ablation(K, w, cache, dev_args, out, torch, per_graph=50, repl
                       tile_waves=4, dequant_mode=mode)
         ms = graph_launch_ms(torch, lambda: K.paged_prefill_causal(w.q, *dev_args, cache, out, w.sm_scale,
                                                                    plan=plan), per_graph, replays)
-        res[name] = {"dequant_mode": mode, "avg_launch_us": round(ms * 1e3, 2),
-                     "TFLOP_s": round(flops / (ms * 1e-3) / 1e12, 1),
-                     "frac": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        res[name] = {"dequant_mode": mode, **tflops_row(flops, ms)}
     return res
 
 
@@ -415,11 +548,17 @@ def bench_achievable(W, dev, torch, np):
     return out
 
 
-def bench_append_stress(K, W, dev, torch, np, iters=12):
-    """65,536-token append (Student-t(3) values, scattered slots).  The 256 MB
-    Infinity Cache is flushed before every timed launch by reading a 512 MiB
-    buffer (untimed; a read leaves no dirty lines to write back during the
-    timed launch); median of 12 launches, HIP events on the launch stream."""
+def bench_append_stress(K, W, dev, torch, np, iters=12, sets=4, rounds=3, replays=2):
+    """65,536-token append (Student-t(3) values, scattered slots), cold, two
+    ways.  (1) The 256 MB Infinity Cache is flushed before every timed launch
+    by reading a 512 MiB buffer (untimed; a read leaves no dirty lines to
+    write back during the timed launch); median of 12 launches, each between
+    its own pair of HIP events (the pair adds a few microseconds).  (2) Back
+    to back without per-launch events: `sets` copies of the K/V input (256 MB
+    each) appended in rotation, `sets` x `rounds` launches captured into one
+    graph and replayed between two events, so that every launch reads inputs
+    untouched for the last sets-1 launches (768 MB of other traffic, more
+    than the Infinity Cache holds)."""
     a = W.append_stress(dev)
     cache = K.PagedCache.empty(a.num_pages, a.page_size, a.num_kv_heads, a.head_dim, dev,
                                a.k_scale, a.v_scale)
@@ -435,44 +574,150 @@ def bench_append_stress(K, W, dev, torch, np, iters=12):
         e1.record()
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1))
+    del flush
     ms = float(np.median(times))
+    inputs = [(a.k, a.v)] + [(a.k.clone(), a.v.clone()) for _ in range(sets - 1)]
+    rot = [0]
+
+    def one():
+        k, v = inputs[rot[0] % sets]
+        rot[0] += 1
+        cache.append(k, v, a.slot_mapping)
+
+    b2b = graph_launch_ms(torch, one, per_graph=sets * rounds, replays=replays)
+    bits = K.read_device_error(dev)
+    if bits:
+        raise SystemExit(f"device error bits {bits} in the append")
     nbytes = append_bytes(a.k.shape[0], a.num_kv_heads, a.head_dim)
     gbs = nbytes / (ms * 1e-3) / 1e9
+    gbs2 = nbytes / (b2b * 1e-3) / 1e9
     return {"workload": a.name, "bound": "hbm", "bytes_per_launch": nbytes,
             "median_launch_us": round(ms * 1e3, 2), "achieved_GBps": round(gbs, 1),
             "peak_GBps": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4), "cache": "cold (flushed)",
+            "back_to_back_avg_us": round(b2b * 1e3, 2), "back_to_back_GBps": round(gbs2, 1),
+            "frac_back_to_back": round(gbs2 / HBM_PEAK_GBS, 4),
+            "target_frac": APPEND_TARGET_FRAC, "meets_target": bool(gbs / HBM_PEAK_GBS >= APPEND_TARGET_FRAC),
             "traffic": _traffic("append_stress")}
 
 
-def cpu_baseline(w, flops_full, hk_s=8):
-    """The oracle (plain C, fp64 attention) on the step's workload: append of
-    all 2048 K/V rows and the prefill of hk_s of the 8 KV heads (all of them
-    by default: the whole step is a few seconds of CPU work); TFLOP/s over
-    the sample's algorithmic flops."""
-    import numpy as np
-    import torch
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
 
-    import oracle as O
-    import workloads as W
-    G = w.num_q_heads // w.num_kv_heads
-    q = W.bf16_bits(w.q[:, : hk_s * G])
-    k, v = W.bf16_bits(w.k), W.bf16_bits(w.v)
-    slots = w.slot_mapping.cpu().numpy()
-    P, ps, H, D = w.num_pages, w.page_size, w.num_kv_heads, w.head_dim
-    threads = O._threads()
+
+def _host_requests(w, reqs, W, np):
+    """Host copies of the requests `reqs` of workload w as a compact batch
+    (own page pool, pages in order), for the oracle."""
+    import torch
+    reqs = list(reqs)
+    ps = w.page_size
+    q_lens, kv_lens = w.q_lens[reqs], w.kv_lens[reqs]
+    npg = (kv_lens + ps - 1) // ps
+    kvp = np.zeros(len(reqs) + 1, np.int32)
+    kvp[1:] = np.cumsum(npg)
+    pt = np.arange(kvp[-1], dtype=np.int32)
+    qo = np.zeros(len(reqs) + 1, np.int32)
+    qo[1:] = np.cumsum(q_lens)
+    qr = np.concatenate([np.arange(w.qo_indptr[r], w.qo_indptr[r + 1]) for r in reqs])
+    kr = np.concatenate([np.arange(w.kv_token_indptr[r], w.kv_token_indptr[r + 1]) for r in reqs])
+    slots = np.concatenate([pt[kvp[i] + np.arange(kv_lens[i]) // ps] * ps + np.arange(kv_lens[i]) % ps
+                            for i in range(len(reqs))]).astype(np.int64)
+    qi, ki = torch.from_numpy(qr).to(w.q.device), torch.from_numpy(kr).to(w.k.device)
+    return dict(q=W.bf16_bits(w.q.index_select(0, qi)), k=W.bf16_bits(w.k.index_select(0, ki)),
+                v=W.bf16_bits(w.v.index_select(0, ki)), qo=qo, kvp=kvp, pt=pt,
+                kvl=kv_lens.astype(np.int32), slots=slots, P=int(kvp[-1]))
+
+
+def _oracle_sample(O, w, reqs, W, np, threads, hk_s=None):
+    """Oracle append + prefill of the requests `reqs` (KV heads [0, hk_s));
+    returns (seconds, sampled flops, sampled (request, query head) pairs)."""
+    s = _host_requests(w, reqs, W, np)
+    H, D, ps = w.num_kv_heads, w.head_dim, w.page_size
+    G = w.num_q_heads // H
+    hk_s = hk_s or H
     t0 = time.perf_counter()
+    c = [np.zeros((s["P"], ps, H, D // 2), np.uint8), np.zeros((s["P"], ps, H, D // 2), np.uint8),
+         np.zeros((s["P"], ps, H, D // 16), np.uint8), np.zeros((s["P"], ps, H, D // 16), np.uint8)]
+    O.append(s["k"], s["v"], s["slots"], w.k_scale, w.v_scale, *c, ps, nthreads=threads)
+    c = [np.ascontiguousarray(x[:, :, :hk_s]) for x in c]
+    q = np.ascontiguousarray(s["q"][:, : hk_s * G])
+    O.prefill(q, s["qo"], s["kvp"], s["pt"], s["kvl"], *c, w.k_scale, w.v_scale, hk_s * G, w.sm_scale,
+              nthreads=threads)
+    sec = time.perf_counter() - t0
+    flops = attention_flops(w.q_lens[list(reqs)], w.kv_lens[list(reqs)], hk_s * G, D)
+    return sec, flops, len(list(reqs)) * hk_s * G
+
+
+def cpu_baseline(w, flops_full, W, dev, torch, np, hk_s=8):
+    """The oracle (plain C, fp64 attention), timed on this host's cores with
+    the oracle's own thread count (capped at 16, this GPU's share of the
+    host):
+      value: the 2048x2048 step (append of all 2048 K/V rows + the prefill
+        of hk_s of the 8 KV heads), TFLOP/s over the sample's flops;
+      append_stress: the full 65,536-token append, GB/s over its bytes;
+      uniform_1024x1024 / ragged_chunked_256: sampled requests, all heads and
+        rows (16 seeded requests; the 8 longest, 8 shortest and 16 random
+        requests), reported as a measured rate per (request, query head) pair
+        and per flop, and an extrapolation of that flop rate to the whole
+        batch (labelled as such)."""
+    import oracle as O
+    threads = O._threads()
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
+    G = w.num_q_heads // w.num_kv_heads
+    sec, flops, _ = _oracle_sample(O, w, [0], W, np, threads, hk_s)
+    res = {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+           "kind": "oracle", "seconds": round(sec, 3),
+           "sample": f"append of all 2048 K/V rows + causal prefill of {hk_s} of 8 KV heads "
+                     f"({hk_s * G} of 32 query heads), fp64 oracle",
+           "host": {"cpu_model": _cpu_model(), "os_cpu_count": os.cpu_count(), "affinity_cpus": affinity,
+                    "threads_used": threads,
+                    "thread_cap": "min(os.cpu_count(), 16): 16 host threads per GPU"}}
+    a = W.append_stress(dev)
+    P, ps, H, D = a.num_pages, a.page_size, a.num_kv_heads, a.head_dim
+    k, v, slots = W.bf16_bits(a.k), W.bf16_bits(a.v), a.slot_mapping.cpu().numpy()
     c = [np.zeros((P, ps, H, D // 2), np.uint8), np.zeros((P, ps, H, D // 2), np.uint8),
          np.zeros((P, ps, H, D // 16), np.uint8), np.zeros((P, ps, H, D // 16), np.uint8)]
-    O.append(k, v, slots, w.k_scale, w.v_scale, *c, ps, nthreads=threads)
-    c = [np.ascontiguousarray(x[:, :, :hk_s]) for x in c]
-    O.prefill(q, w.qo_indptr, w.kv_indptr, w.page_table, w.kv_lens, *c, w.k_scale, w.v_scale,
-              hk_s * G, w.sm_scale, nthreads=threads)
-    sec = time.perf_counter() - t0
-    flops = flops_full * hk_s // w.num_kv_heads
-    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "seconds": round(sec, 3),
-            "sample": f"append of all 2048 K/V rows + causal prefill of {hk_s} of 8 KV heads "
-                      f"({hk_s * G} of 32 query heads), fp64 oracle"}
+    t0 = time.perf_counter()
+    O.append(k, v, slots, a.k_scale, a.v_scale, *c, ps, nthreads=threads)
+    asec = time.perf_counter() - t0
+    nbytes = append_bytes(a.k.shape[0], H, D)
+    res["append_stress"] = {"seconds": round(asec, 3), "GB_s": round(nbytes / asec / 1e9, 3),
+                            "sample": "the whole 65,536-token append"}
+    del a, k, v, c
+    for name, mkw, pick in (
+            ("uniform_1024x1024", W.uniform_batch_1k,
+             lambda wl: np.random.default_rng(7).choice(wl.batch, 16, replace=False)),
+            ("ragged_chunked_256", W.ragged_chunked,
+             lambda wl: _ragged_pick(wl, np))):
+        wl = mkw(dev)
+        reqs = [int(r) for r in pick(wl)]
+        sec, flops, pairs = _oracle_sample(O, wl, reqs, W, np, threads)
+        full = attention_flops(wl.q_lens, wl.kv_lens, wl.num_q_heads, wl.head_dim)
+        rate = flops / sec
+        res[name] = {"seconds": round(sec, 3), "sampled_requests": len(reqs),
+                     "sampled_request_head_pairs": pairs, "sampled_flops": flops,
+                     "TFLOP_s": round(rate / 1e12, 6),
+                     "seconds_per_request_head_pair": round(sec / pairs, 5),
+                     "extrapolated_full_batch_seconds": round(full / rate, 1),
+                     "extrapolation": "the sample's measured flop rate applied to the whole batch's "
+                                      f"{full} flops (not measured)"}
+        del wl
+        torch.cuda.empty_cache()
+    return res
+
+
+def _ragged_pick(w, np):
+    order = np.argsort(w.kv_lens, kind="stable")
+    rest = np.setdiff1d(np.arange(w.batch), np.concatenate([order[:8], order[-8:]]))
+    return np.concatenate([order[-8:], order[:8], np.random.default_rng(3).choice(rest, 16, replace=False)])
 
 
 if __name__ == "__main__":

@@ -291,6 +291,13 @@ class Plan:
         if schedule:
             self.struct.schedule = int(schedule)
         self.qo_host, self.kv_lens_host, self.kv_indptr_host = qo, kvl, kvp
+        # page-table entries the batch's requests own (checked against the
+        # device page table's size at every call)
+        if kvp is not None and kvp.numel() == kvl.numel() + 1:
+            self.pages_needed = int(kvp[-1]) if kvp.numel() else 0
+        else:
+            self.pages_needed = int(((kvl.to(torch.int64) + page_size - 1) // page_size).sum()) \
+                if kvl.numel() else 0
         self._workspace = {}
 
     def __getattr__(self, name):
@@ -387,6 +394,8 @@ class DecodePlan:
                                        page_size, chunk_len, ctypes.byref(self.struct)),
                "nvfp4_decode_plan")
         self.kv_lens_host = kvl
+        self.pages_needed = int(((kvl.to(torch.int64) + page_size - 1) // page_size).sum()) \
+            if kvl.numel() else 0
         self._workspace = {}
 
     def __getattr__(self, name):
@@ -446,13 +455,7 @@ def _check_batch_arrays(plan, qo_indptr, kv_indptr, kv_lens, page_table):
         raise ValueError(f"kv_indptr must have batch + 1 = {B + 1} entries")
     if kv_lens.numel() != B:
         raise ValueError(f"kv_lens must have batch = {B} entries")
-    kvp = getattr(plan, "kv_indptr_host", None)
-    need = int(kvp[-1]) if kvp is not None and kvp.numel() == B + 1 else None
-    if need is None:
-        # pages each request needs, from the plan's host lengths
-        kvl = plan.kv_lens_host
-        ps = plan.page_size
-        need = int(((kvl.to(torch.int64) + ps - 1) // ps).sum()) if kvl.numel() else 0
+    need = plan.pages_needed
     if page_table.numel() < need:
         raise ValueError(f"page_table has {page_table.numel()} entries; the batch's requests "
                          f"own {need}")

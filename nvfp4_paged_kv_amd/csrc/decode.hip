@@ -47,6 +47,16 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr f16x2 kOnes = {(_Float16)1.0f, (_Float16)1.0f};
 constexpr float kRescaleSlack = 8.0f;  // log2 units, as in the prefill
+
+// As in the prefill: rows whose scores can reach 2^24 in log2 units (c times
+// the largest raw score, head_dim x 2^15 x 2688) form p = exp2((s - m) c) with
+// the reference m in raw score units; others p = exp2(fma(s, c, -m)) with m
+// in log2 units.  The choice is per query head, the same on every chunk.
+template <int D>
+__device__ __forceinline__ bool exact_scores(float c) {
+  constexpr float kMaxRaw = (float)D * 32768.0f * 2688.0f;
+  return c * kMaxRaw >= 16777216.0f;
+}
 constexpr int kWaves = 8;              // independent waves per workgroup
 
 template <int D>
@@ -215,7 +225,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   f32x4 o[C::NDB];
 #pragma unroll
   for (int i = 0; i < C::NDB; ++i) o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // reference max: log2 units, or raw score units on a wave whose query heads
+  // need the exact score form
   float m_run = -__builtin_inff(), l_run = 0.0f;
+  const bool exact = __any(row < G && exact_scores<D>(cscale));
 
   // V^T transpose-read addressing: lane t of each 16-lane group (quarter qq)
   // points at 4 consecutive head_dim values of key 4qq + t/4 (+16, +32m).
@@ -270,10 +283,18 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
       for (int r = 0; r < 4; ++r) mx = __builtin_fmaxf(mx, s[kb][r]);
     mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
     mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_tile = mx * cscale;
-    const bool grow = m_tile > m_run + kRescaleSlack;
-    const float m_new = grow ? m_tile : m_run;
-    const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+    float m_new, alpha;
+    bool grow;
+    if (exact) {
+      grow = (mx - m_run) * cscale > kRescaleSlack;  // (-inf) - (-inf): NaN, no growth
+      m_new = grow ? mx : m_run;
+      alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * cscale) : 1.0f;
+    } else {
+      const float m_tile = mx * cscale;
+      grow = m_tile > m_run + kRescaleSlack;
+      m_new = grow ? m_tile : m_run;
+      alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+    }
     m_run = m_new;
     l_run *= alpha;
     if (__any(grow)) {
@@ -291,8 +312,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int r2 = 0; r2 < 2; ++r2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m + h][2 * r2], cscale, -m_new));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * m + h][2 * r2 + 1], cscale, -m_new));
+          const float x0 = s[2 * m + h][2 * r2], x1 = s[2 * m + h][2 * r2 + 1];
+          const float p0 = __builtin_amdgcn_exp2f(exact ? (x0 - m_new) * cscale : __builtin_fmaf(x0, cscale, -m_new));
+          const float p1 = __builtin_amdgcn_exp2f(exact ? (x1 - m_new) * cscale : __builtin_fmaf(x1, cscale, -m_new));
           const f16x2 pp = {(_Float16)p0, (_Float16)p1};
           l_run = __builtin_amdgcn_fdot2(pp, kOnes, l_run, false);
           pw[2 * h + r2] = __builtin_bit_cast(uint32_t, pp);
@@ -340,6 +362,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
     if (qq == 0) {
       part[D] = m_run;
       part[D + 1] = l_tot;
+      part[D + 2] = exact ? cscale : 0.0f;  // how the merge compares references
     }
   }
 }
@@ -365,6 +388,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_merge_kernel(DecodeArgs a)
   float M = -__builtin_inff();
   float acc[E] = {};
   float L = 0.0f;
+  // references in raw score units (times the row's scale c) or in log2 units
+  const float c = base[D + 2];
+  auto ratio = [&](float from, float to) {
+    return __builtin_amdgcn_exp2f(c > 0.0f ? (from - to) * c : from - to);
+  };
   for (int c0 = 0; c0 < n; c0 += U) {
     float mc[U], lc[U], oc[U][E];
 #pragma unroll
@@ -379,7 +407,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_merge_kernel(DecodeArgs a)
 #pragma unroll
     for (int i = 0; i < U; ++i) Mb = __builtin_fmaxf(Mb, mc[i]);
     if (c0 > 0 && Mb > M) {  // the reference moves: rescale what is summed
-      const float r = __builtin_amdgcn_exp2f(M - Mb);
+      const float r = ratio(M, Mb);
       L *= r;
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[e] *= r;
@@ -388,7 +416,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_merge_kernel(DecodeArgs a)
 #pragma unroll
     for (int i = 0; i < U; ++i) {
       if (c0 + i >= n) break;
-      const float f = __builtin_amdgcn_exp2f(mc[i] - M);
+      const float f = ratio(mc[i], M);
       L = __builtin_fmaf(lc[i], f, L);
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(oc[i][e], f, acc[e]);

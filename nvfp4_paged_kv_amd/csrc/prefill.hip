@@ -104,6 +104,21 @@ struct Cfg {
 // against a max that may lag the true running max by up to this much.
 constexpr float kRescaleSlack = 8.0f;
 
+// Scores are formed in two ways.  Normally p = exp2(fma(s, c, -m)) with the
+// reference m in log2 units (s the raw matrix-core score, c the row's score
+// scale): m's rounding error is a factor common to every p of the row and
+// cancels.  When |s c| can reach 2^24 (a row of enormous queries), half an
+// ulp of m is no longer small and exp2 would overflow; such rows use the
+// exact form p = exp2((s - m) c) with m in raw score units.  A row may take
+// the exact form when c times the largest possible raw score (head_dim x
+// 2^15 x 2688: a query rescaled below 2^15 times the largest staged key,
+// 6 x 448) reaches 2^24.
+template <int D>
+__device__ __forceinline__ bool exact_scores(float c) {
+  constexpr float kMaxRaw = (float)D * 32768.0f * 2688.0f;
+  return c * kMaxRaw >= 16777216.0f;
+}
+
 // Two E2M1 codes (byte SEL of x) times one E4M3 block scale, as an f16 pair:
 // the products (at most 5 significant bits, magnitudes 2^-10 .. 2688) are
 // exact in f16, so the packed f16 multiply rounds nothing.
@@ -398,6 +413,195 @@ struct TileStager {
   }
 };
 
+// The work item of workgroup `tile`: request b, KV head hk, Q tile qt, and
+// the KV tile range [jt_begin, jt_end) (the whole range unless the item is
+// one chunk of a split Q tile; split: -1, or (split id << 10) | (chunk << 5)
+// | chunks).
+struct Item {
+  int b, hk, qt, jt_begin, jt_end, split;
+};
+__device__ __forceinline__ Item decode_item(const PrefillArgs& a, uint32_t tile) {
+  Item it;
+  it.jt_begin = 0;
+  it.jt_end = 0x7FFFFFFF;
+  it.split = -1;
+  if (a.worklist) {
+    const int4 e = a.worklist[tile];
+    it.b = e.x;
+    it.qt = e.y / a.Hk;
+    it.hk = e.y - it.qt * a.Hk;
+    it.jt_begin = (uint32_t)e.z >> 16;
+    it.jt_end = e.z & 0xFFFF;
+    it.split = e.w;
+    return it;
+  }
+  const uint32_t bh_n = (uint32_t)a.B * a.Hk;
+  uint32_t bh, qrev;
+  if (a.order == kOrderHeaviest) {
+    // heaviest Q tiles of every (request, head) first
+    qrev = tile / bh_n;
+    bh = tile - qrev * bh_n;
+    // When the whole grid is resident at once, workgroup p and p + grid/2
+    // share a CU: the second half walks the remaining tiles lightest first
+    // so that every CU gets one heavy and one light tile.
+    const uint32_t half = (a.QT + 1) / 2;
+    if (a.snake && qrev >= half) qrev = a.QT - 1 - (qrev - half);
+  } else if (a.order == kOrderStream) {
+    // stream-major: XCD x (blockIdx % nxcd) owns a contiguous range of
+    // (request, head) streams, each walked heaviest tile first
+    const uint32_t nx = a.nxcd, x = tile % nx, s = tile / nx;
+    const uint32_t per = a.num_tiles / nx, rem = a.num_tiles % nx;
+    const uint32_t L = x * per + (x < rem ? x : rem) + s;
+    bh = L / a.QT;
+    qrev = L - bh * a.QT;
+  } else {
+    // request order: (request, head) streams in order, each one's Q tiles
+    // lightest first -- no reordering at all
+    bh = tile / a.QT;
+    qrev = a.QT - 1 - (tile - bh * a.QT);
+  }
+  it.b = bh / a.Hk;
+  it.hk = bh - it.b * a.Hk;
+  it.qt = a.QT - 1 - qrev;
+  return it;
+}
+
+// Q^T operand fragments of one query row (the lane's row; hh selects the
+// half of each 16-element k-step): lane holds Q[row][16c + 8hh .. +7], in f16
+// after an exact power-of-two rescale of the row: bf16 values have 8
+// significant bits, and the row's largest magnitude goes to [2^14, 2^15), so
+// every value within 2^-28 of it stays a normal f16.  The row's scale comes
+// back in its score scale, returned (scores -> log2 domain).  DQ 3: bf16
+// fragments as they are.
+template <int D, int DQ>
+__device__ __forceinline__ float load_q(const uint16_t* qrow, int hh, float score_scale, f16x8 (&qf)[D / 16]) {
+  constexpr int NDC = D / 16;
+  u32x4 qw[NDC];
+  uint32_t am = 0;  // largest |bf16| bit pattern of the row
+#pragma unroll
+  for (int c = 0; c < NDC; ++c) {
+    qw[c] = *(const u32x4*)(qrow + c * 16 + hh * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) am = max(am, max(qw[c][e] & 0x7FFFu, (qw[c][e] >> 16) & 0x7FFFu));
+  }
+  am = max(am, (uint32_t)__shfl_xor((int)am, 32));  // the row's other half
+  const int sh = DQ == 3 ? 0 : am >= 0x80u ? min(max((int)(am >> 7) - 127 - 14, -100), 113) : 0;
+  const float down = u2f((uint32_t)(127 - sh) << 23);  // 2^-sh
+#pragma unroll
+  for (int c = 0; c < NDC; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (DQ != 3) {  // (bf16 matrix instructions take the bf16 bits as they are)
+        const f16x2 h = {(_Float16)(u2f(qw[c][e] << 16) * down), (_Float16)(u2f(qw[c][e] & 0xFFFF0000u) * down)};
+        qw[c][e] = __builtin_bit_cast(uint32_t, h);
+      }
+    }
+#pragma unroll
+  for (int c = 0; c < NDC; ++c) __builtin_memcpy(&qf[c], &qw[c], 16);
+  // Consume the Q fragments here, so their load waits are placed before the
+  // KV loop rather than inside it (where they would also wait for the
+  // prefetch of the next tile).
+#pragma unroll
+  for (int c = 0; c < NDC; ++c) asm volatile("" ::"v"(qf[c]));
+  return score_scale * u2f((uint32_t)(127 + sh) << 23);
+}
+
+// ---- split Q tile: all but the last chunk to arrive publish a partial
+// (unnormalized O^T, reference max, sum); the last one merges them all in
+// chunk order (symmetric: the result does not depend on arrival order).
+// The partials move through device-coherent loads and stores and the
+// counters through relaxed device-scope atomics: no cache-wide write-back
+// or invalidate, which would evict the KV tiles other work-groups on the
+// same L2 are reading.  Every thread of the workgroup calls this (it has
+// barriers); `active` threads (the ones holding the tile's O^T; ltid in
+// [0, 2 ROWS) their index in the partial's layout, 64 per 32-row block)
+// move data.  Returns false when this workgroup published its partial and
+// is done.
+template <int D, int ROWS>
+__device__ __forceinline__ bool split_merge(const PrefillArgs& a, int split, int tid, int ltid, bool active,
+                                            int r, bool exact, float cscale, float& m_run, float& l_tot,
+                                            f32x16 (&o)[D / 32]) {
+  constexpr int NDB = D / 32, NT = 2 * ROWS;
+  const int sid = split >> 10, chunk = (split >> 5) & 31, nch = split & 31;
+  int* arrive = a.counters + 2 * sid;
+  __shared__ int s_prior;
+  if (tid == 0) s_prior = __hip_atomic_fetch_add(arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int prior = s_prior;
+  const __amdgpu_buffer_rsrc_t parts = coherent_rsrc(
+      a.partials + (int64_t)sid * a.max_chunks * a.partial_floats,
+      (uint32_t)(a.max_chunks * a.partial_floats * 4));
+  const int ml_base = ROWS * D;  // floats: O^T, then m per row, then l per row
+  const int hh = (ltid >> 5) & 1;
+  if (prior < nch - 1) {
+    if (active) {
+      const int cb = chunk * (int)a.partial_floats * 4;  // byte offset of this chunk
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+          coherent_store4(parts, cb + ((db * 4 + i4) * NT + ltid) * 16,
+                          (f32x4){o[db][4 * i4], o[db][4 * i4 + 1], o[db][4 * i4 + 2], o[db][4 * i4 + 3]});
+      if (hh == 0) {
+        coherent_store1(parts, cb + (ml_base + r) * 4, m_run);
+        coherent_store1(parts, cb + (ml_base + ROWS + r) * 4, l_tot);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial is written
+    __syncthreads();
+    if (tid == 0) __hip_atomic_fetch_add(arrive + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return false;
+  }
+  // last to arrive: the other chunks have all arrived and are finishing
+  // their partials; wait (bounded) until all of them are published
+  if (tid == 0) {
+    int spins = 0;
+    while (__hip_atomic_load(arrive + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nch - 1) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins == (1 << 22)) {
+        atomicOr(a.err, (uint32_t)NVFP4KV_DEV_SPLIT_TIMEOUT);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  if (!active) return true;
+  float m_all = m_run;
+  for (int c = 0; c < nch; ++c)
+    if (c != chunk)
+      m_all = __builtin_fmaxf(m_all, coherent_load1(parts, (c * (int)a.partial_floats + ml_base + r) * 4));
+  const float m_ref = m_all == -__builtin_inff() ? 0.0f : m_all;
+  f32x16 acc[NDB];
+  float l_acc = 0.0f;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = (f32x16){};
+  // Identical arithmetic for the chunk held in registers and the chunks
+  // read back (explicit FMAs), so the bits do not depend on which chunk
+  // arrived last.
+  for (int c = 0; c < nch; ++c) {
+    const int cb = c * (int)a.partial_floats * 4;
+    const bool mine = c == chunk;
+    const float mc = mine ? m_run : coherent_load1(parts, cb + (ml_base + r) * 4);
+    const float lc = mine ? l_tot : coherent_load1(parts, cb + (ml_base + ROWS + r) * 4);
+    const float f = __builtin_amdgcn_exp2f(exact ? (mc - m_ref) * cscale : mc - m_ref);
+    l_acc = __builtin_fmaf(lc, f, l_acc);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        f32x4 v = {o[db][4 * i4], o[db][4 * i4 + 1], o[db][4 * i4 + 2], o[db][4 * i4 + 3]};
+        if (!mine) v = coherent_load4(parts, cb + ((db * 4 + i4) * NT + ltid) * 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[db][4 * i4 + e] = __builtin_fmaf(v[e], f, acc[db][4 * i4 + e]);
+      }
+  }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = acc[db];
+  l_tot = l_acc;
+  m_run = m_all;
+  return true;
+}
+
 template <int D, int G, int W, bool PA, int DQ>
 __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   using C = Cfg<D, G, W>;
@@ -408,49 +612,9 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, hh = lane >> 5;
 
-  // ---- which (request, KV head, Q tile, KV range) this workgroup computes
-  int b, hk, qt;
-  int jt_begin = 0, jt_end = 0x7FFFFFFF, split = -1;
+  const Item it = decode_item(a, blockIdx.x);
+  const int b = it.b, hk = it.hk, qt = it.qt, jt_begin = it.jt_begin, jt_end = it.jt_end, split = it.split;
   const uint32_t tile = blockIdx.x;
-  if (a.worklist) {
-    const int4 e = a.worklist[tile];
-    b = e.x;
-    qt = e.y / a.Hk;
-    hk = e.y - qt * a.Hk;
-    jt_begin = (uint32_t)e.z >> 16;
-    jt_end = e.z & 0xFFFF;
-    split = e.w;  // -1, or (split id << 10) | (chunk << 5) | chunks
-  } else {
-    const uint32_t bh_n = (uint32_t)a.B * a.Hk;
-    uint32_t bh, qrev;
-    if (a.order == kOrderHeaviest) {
-      // heaviest Q tiles of every (request, head) first
-      qrev = tile / bh_n;
-      bh = tile - qrev * bh_n;
-      // When the whole grid is resident at once, workgroup p and p + grid/2
-      // share a CU: the second half walks the remaining tiles lightest first
-      // so that every CU gets one heavy and one light tile.
-      const uint32_t half = (a.QT + 1) / 2;
-      if (a.snake && qrev >= half) qrev = a.QT - 1 - (qrev - half);
-    } else if (a.order == kOrderStream) {
-      // stream-major: XCD x (blockIdx % nxcd) owns a contiguous range of
-      // (request, head) streams, each walked heaviest tile first
-      const uint32_t nx = a.nxcd, x = tile % nx, s = tile / nx;
-      const uint32_t per = a.num_tiles / nx, rem = a.num_tiles % nx;
-      const uint32_t L = x * per + (x < rem ? x : rem) + s;
-      bh = L / a.QT;
-      qrev = L - bh * a.QT;
-    } else {
-      // request order: (request, head) streams in order, each one's Q tiles
-      // lightest first -- no reordering at all
-      bh = tile / a.QT;
-      qrev = a.QT - 1 - (tile - bh * a.QT);
-    }
-    b = bh / a.Hk;
-    hk = bh - b * a.Hk;
-    qt = a.QT - 1 - qrev;
-  }
-
   const int q_begin = a.qo[b];
   const int Lq = a.qo[b + 1] - q_begin;
   const int Lk = a.kvl[b];
@@ -481,49 +645,17 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   const float gk = *a.kscale, gv = *a.vscale;
   if (tile == 0 && tid == 0 && !(scale_ok(gk) && scale_ok(gv)))
     atomicOr(a.err, (uint32_t)NVFP4KV_DEV_BAD_SCALE_ATTN);
-  // ---- Q^T operand fragments: lane holds Q[row][16c + 8hh .. +7], in f16
-  // after an exact power-of-two rescale of the row: bf16 values have 8
-  // significant bits, and the row's largest magnitude goes to [2^14, 2^15),
-  // so every value within 2^-28 of it stays a normal f16.  The row's scale
-  // comes back in its score scale.
   f16x8 qf[C::NDC];
-  float cscale;  // scores -> log2 domain
-  {
-    const uint16_t* qrow = a.q + ((int64_t)(q_begin + (row_valid ? tok : q0)) * a.Hq + hq) * D;
-    u32x4 qw[C::NDC];
-    uint32_t am = 0;  // largest |bf16| bit pattern of the row
-#pragma unroll
-    for (int c = 0; c < C::NDC; ++c) {
-      qw[c] = *(const u32x4*)(qrow + c * 16 + hh * 8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) am = max(am, max(qw[c][e] & 0x7FFFu, (qw[c][e] >> 16) & 0x7FFFu));
-    }
-    am = max(am, (uint32_t)__shfl_xor((int)am, 32));  // the row's other half
-    const int sh = DQ == 3 ? 0 : am >= 0x80u ? min(max((int)(am >> 7) - 127 - 14, -100), 113) : 0;
-    const float down = u2f((uint32_t)(127 - sh) << 23);  // 2^-sh
-    cscale = a.sm_scale_log2 * gk * u2f((uint32_t)(127 + sh) << 23);
-#pragma unroll
-    for (int c = 0; c < C::NDC; ++c)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (DQ != 3) {  // (bf16 matrix instructions take the bf16 bits as they are)
-          const f16x2 h = {(_Float16)(u2f(qw[c][e] << 16) * down), (_Float16)(u2f(qw[c][e] & 0xFFFF0000u) * down)};
-          qw[c][e] = __builtin_bit_cast(uint32_t, h);
-        }
-      }
-#pragma unroll
-    for (int c = 0; c < C::NDC; ++c) __builtin_memcpy(&qf[c], &qw[c], 16);
-    // Consume the Q fragments here, so their load waits are placed before the
-    // KV loop rather than inside it (where they would also wait for the
-    // prefetch of the next tile).
-#pragma unroll
-    for (int c = 0; c < C::NDC; ++c) asm volatile("" ::"v"(qf[c]));
-  }
+  const float cscale = load_q<D, DQ>(a.q + ((int64_t)(q_begin + (row_valid ? tok : q0)) * a.Hq + hq) * D, hh,
+                                     a.sm_scale_log2 * gk, qf);
 
   f32x16 o[C::NDB];
 #pragma unroll
   for (int i = 0; i < C::NDB; ++i) o[i] = (f32x16){};
+  // reference max: log2 units, or raw score units on a wave whose rows need
+  // the exact score form (the same on every chunk of a split tile)
   float m_run = -__builtin_inff(), l_run = 0.0f;
+  const bool exact = __any(exact_scores<D>(cscale));
 
   // V^T operand addressing (transpose reads): lane t of each 16-lane group
   // points at 4 consecutive head_dim values of one key.
@@ -544,8 +676,9 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   // One KV tile j: S^T = K Q^T from buffer j&1; dequantize tile j+1 into the
   // other buffer (VALU work that runs beside the matrix cores); prefetch tile
   // j+2; (mask), online softmax, O^T += V^T P^T; one barrier.
-  auto tile_step = [&](const int jt, auto masked) {
+  auto tile_step = [&](const int jt, auto masked, auto exact_form) {
     constexpr bool MASK = decltype(masked)::value;
+    constexpr bool EXACT = decltype(exact_form)::value;
     const uint8_t* const sK = smem + (jt & 1) * STG;
     const uint8_t* const vbase = sK + voff;
     pin_jobs<D, G, W>(job);
@@ -614,10 +747,18 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     // Lazy rescaling: the reference max moves only when the tile's max
     // exceeds it by more than kRescaleSlack (log2 units), so p stays below
     // 2^kRescaleSlack and the O^T rescale is skipped on most tiles.
-    const float m_tile = mx * cscale;
-    const bool grow = m_tile > m_run + kRescaleSlack;
-    const float m_new = grow ? m_tile : m_run;
-    const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+    float m_new, alpha;
+    bool grow;
+    if constexpr (EXACT) {
+      grow = (mx - m_run) * cscale > kRescaleSlack;  // (-inf) - (-inf): NaN, no growth
+      m_new = grow ? mx : m_run;
+      alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * cscale) : 1.0f;
+    } else {
+      const float m_tile = mx * cscale;
+      grow = m_tile > m_run + kRescaleSlack;
+      m_new = grow ? m_tile : m_run;
+      alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+    }
     m_run = m_new;
     l_run *= alpha;
     if (__any(grow)) {
@@ -637,9 +778,12 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     // read VA instructions ahead.
     constexpr int NPV = 4 * C::NDB, VA = 3;
     uint32_t pw[4][4];
+    auto pexp = [&](float x) {
+      return __builtin_amdgcn_exp2f(EXACT ? (x - m_sub) * cscale : __builtin_fmaf(x, cscale, -m_sub));
+    };
     auto exps = [&](int kc, int j) {  // pair j of chunk kc
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kc >> 1][8 * (kc & 1) + 2 * j], cscale, -m_sub));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kc >> 1][8 * (kc & 1) + 2 * j + 1], cscale, -m_sub));
+      const float p0 = pexp(s[kc >> 1][8 * (kc & 1) + 2 * j]);
+      const float p1 = pexp(s[kc >> 1][8 * (kc & 1) + 2 * j + 1]);
       if constexpr (DQ == 3) {
         const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
         l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnesBf16x2, l_run, false);
@@ -683,93 +827,19 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   };
   // KV tiles entirely at or below the first row's last key need no mask.
   const int n_full = min(ntiles, (kend_min + 1) / C::BN);
-  int jt = jt_begin;
-  for (; jt < n_full; ++jt) tile_step(jt, std::false_type{});
-  for (; jt < ntiles; ++jt) tile_step(jt, std::true_type{});
+  auto kv_loop = [&](auto exact_form) {
+    int jt = jt_begin;
+    for (; jt < n_full; ++jt) tile_step(jt, std::false_type{}, exact_form);
+    for (; jt < ntiles; ++jt) tile_step(jt, std::true_type{}, exact_form);
+  };
+  if (exact)
+    kv_loop(std::true_type{});
+  else
+    kv_loop(std::false_type{});
   if (page_bad) atomicOr(a.err, (uint32_t)NVFP4KV_DEV_PAGE_OOB);
 
   float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (split >= 0) {
-    // ---- split Q tile: all but the last chunk to arrive publish a partial
-    // (unnormalized O^T, reference max, sum); the last one merges them all in
-    // chunk order (symmetric: the result does not depend on arrival order).
-    // The partials move through device-coherent loads and stores and the
-    // counters through relaxed device-scope atomics: no cache-wide write-back
-    // or invalidate, which would evict the KV tiles other work-groups on the
-    // same L2 are reading.
-    const int sid = split >> 10, chunk = (split >> 5) & 31, nch = split & 31;
-    int* arrive = a.counters + 2 * sid;
-    __shared__ int s_prior;
-    if (tid == 0) s_prior = __hip_atomic_fetch_add(arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const int prior = s_prior;
-    const __amdgpu_buffer_rsrc_t parts = coherent_rsrc(
-        a.partials + (int64_t)sid * a.max_chunks * a.partial_floats,
-        (uint32_t)(a.max_chunks * a.partial_floats * 4));
-    const int ml_base = 32 * W * D;  // floats: O^T, then m per row, then l per row
-    if (prior < nch - 1) {
-      const int cb = chunk * (int)a.partial_floats * 4;  // byte offset of this chunk
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4)
-          coherent_store4(parts, cb + ((db * 4 + i4) * C::NT + tid) * 16,
-                          (f32x4){o[db][4 * i4], o[db][4 * i4 + 1], o[db][4 * i4 + 2], o[db][4 * i4 + 3]});
-      if (hh == 0) {
-        coherent_store1(parts, cb + (ml_base + r) * 4, m_run);
-        coherent_store1(parts, cb + (ml_base + 32 * W + r) * 4, l_tot);
-      }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial is written
-      __syncthreads();
-      if (tid == 0) __hip_atomic_fetch_add(arrive + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return;
-    }
-    // last to arrive: the other chunks have all arrived and are finishing
-    // their partials; wait (bounded) until all of them are published
-    if (tid == 0) {
-      int spins = 0;
-      while (__hip_atomic_load(arrive + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nch - 1) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++spins == (1 << 22)) {
-          atomicOr(a.err, (uint32_t)NVFP4KV_DEV_SPLIT_TIMEOUT);
-          break;
-        }
-      }
-    }
-    __syncthreads();
-    float m_all = m_run;
-    for (int c = 0; c < nch; ++c)
-      if (c != chunk)
-        m_all = __builtin_fmaxf(m_all, coherent_load1(parts, (c * (int)a.partial_floats + ml_base + r) * 4));
-    const float m_ref = m_all == -__builtin_inff() ? 0.0f : m_all;
-    f32x16 acc[C::NDB];
-    float l_acc = 0.0f;
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) acc[db] = (f32x16){};
-    // Identical arithmetic for the chunk held in registers and the chunks
-    // read back (explicit FMAs), so the bits do not depend on which chunk
-    // arrived last.
-    for (int c = 0; c < nch; ++c) {
-      const int cb = c * (int)a.partial_floats * 4;
-      const bool mine = c == chunk;
-      const float mc = mine ? m_run : coherent_load1(parts, cb + (ml_base + r) * 4);
-      const float lc = mine ? l_tot : coherent_load1(parts, cb + (ml_base + 32 * W + r) * 4);
-      const float f = __builtin_amdgcn_exp2f(mc - m_ref);
-      l_acc = __builtin_fmaf(lc, f, l_acc);
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          f32x4 v = {o[db][4 * i4], o[db][4 * i4 + 1], o[db][4 * i4 + 2], o[db][4 * i4 + 3]};
-          if (!mine) v = coherent_load4(parts, cb + ((db * 4 + i4) * C::NT + tid) * 16);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[db][4 * i4 + e] = __builtin_fmaf(v[e], f, acc[db][4 * i4 + e]);
-        }
-    }
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) o[db] = acc[db];
-    l_tot = l_acc;
-  }
+  if (split >= 0 && !split_merge<D, 32 * W>(a, split, tid, tid, true, r, exact, cscale, m_run, l_tot, o)) return;
 
   // ---- epilogue: O / l * g_v -> bf16; lane holds O^T[d][row n]
   const float inv = gv / l_tot;
