@@ -30,6 +30,8 @@
 // and g_v into the output.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "nvfp4kv_codec.hpp"
 #include "nvfp4kv_internal.hpp"
 
@@ -240,6 +242,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   load(0, pg, raw);
   lookup(1, pg_next);
 
+  // the KV loop, in one copy per score form (the choice is fixed per wave)
+  auto kv_loop = [&](auto exact_form) {
+  constexpr bool EXACT = decltype(exact_form)::value;
   for (int t = 0; t < ntiles; ++t) {
     Raw<D> nraw;
     load(t + 1, pg_next, nraw);  // past the last tile: clamped, unused
@@ -285,7 +290,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
     mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
     float m_new, alpha;
     bool grow;
-    if (exact) {
+    if constexpr (EXACT) {
       grow = (mx - m_run) * cscale > kRescaleSlack;  // (-inf) - (-inf): NaN, no growth
       m_new = grow ? mx : m_run;
       alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * cscale) : 1.0f;
@@ -313,8 +318,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int r2 = 0; r2 < 2; ++r2) {
           const float x0 = s[2 * m + h][2 * r2], x1 = s[2 * m + h][2 * r2 + 1];
-          const float p0 = __builtin_amdgcn_exp2f(exact ? (x0 - m_new) * cscale : __builtin_fmaf(x0, cscale, -m_new));
-          const float p1 = __builtin_amdgcn_exp2f(exact ? (x1 - m_new) * cscale : __builtin_fmaf(x1, cscale, -m_new));
+          const float p0 = __builtin_amdgcn_exp2f(EXACT ? (x0 - m_new) * cscale : __builtin_fmaf(x0, cscale, -m_new));
+          const float p1 = __builtin_amdgcn_exp2f(EXACT ? (x1 - m_new) * cscale : __builtin_fmaf(x1, cscale, -m_new));
           const f16x2 pp = {(_Float16)p0, (_Float16)p1};
           l_run = __builtin_amdgcn_fdot2(pp, kOnes, l_run, false);
           pw[2 * h + r2] = __builtin_bit_cast(uint32_t, pp);
@@ -338,6 +343,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) pg[kb] = pg_next[kb];
   }
+  };
+  if (exact)
+    kv_loop(std::true_type{});
+  else
+    kv_loop(std::false_type{});
   if (page_bad) atomicOr(a.err, (uint32_t)NVFP4KV_DEV_PAGE_OOB);
 
   // ---- the head's sum over its 4 quarter lanes; then output or partial
