@@ -16,7 +16,8 @@
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless the name ends in `_host`.  All
  *     buffers belong to the caller; the library allocates nothing and keeps no
- *     state besides a per-device property cache.
+ *     state besides a per-device property cache and, for
+ *     paged_prefill_causal_noalloc, one static device array per GPU.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues work on it and returns: none synchronizes the host, except
  *     nvfp4kv_read_device_error, which exists to do exactly that.
@@ -249,6 +250,28 @@ int paged_prefill_causal(const void* q, const int32_t* qo_indptr, const int32_t*
                          const nvfp4kv_cache* caches, void* out, float sm_scale,
                          const nvfp4kv_prefill_plan* plan, void* workspace,
                          int64_t workspace_bytes, uint32_t* dev_error, void* stream);
+
+/*
+ * paged_prefill_causal_noalloc -- for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): paged_prefill_causal without the workspace argument.
+ * The work list, split counters and partials go to a library-owned device
+ * array of NVFP4KV_NOALLOC_SCRATCH_BYTES on each GPU (held from the first
+ * use of the library on that GPU until the process ends); the call itself
+ * allocates nothing.  A plan whose workspace_bytes exceed that size returns
+ * NVFP4KV_EWORKSPACE before anything is enqueued.  The array keeps the last
+ * call's contents; each call initialises what it reads (work list, zeroed
+ * counters).  All calls on one GPU share the array: calls that overlap in
+ * time on one GPU (different streams, or different host threads) race and
+ * must not be issued.  Other arguments, errors and results are those of
+ * paged_prefill_causal.
+ */
+#define NVFP4KV_NOALLOC_SCRATCH_BYTES (64ll << 20)
+int paged_prefill_causal_noalloc(const void* q, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                                 const int32_t* page_table, const int32_t* kv_lens,
+                                 const nvfp4kv_cache* caches, void* out, float sm_scale,
+                                 const nvfp4kv_prefill_plan* plan, uint32_t* dev_error,
+                                 void* stream);
 
 /* Host-side launch plan of one decode batch (filled by nvfp4_decode_plan). */
 typedef struct {

@@ -31,7 +31,7 @@ DEV_BAD_K_SCALE, DEV_BAD_V_SCALE, DEV_SLOT_OOB, DEV_PAGE_OOB, DEV_BAD_SCALE_ATTN
 DEV_SPLIT_TIMEOUT = 32
 
 ENTRY_POINTS = ("nvfp4_append_paged_kv", "nvfp4_prefill_plan", "paged_prefill_causal",
-                "nvfp4_decode_plan", "paged_decode",
+                "paged_prefill_causal_noalloc", "nvfp4_decode_plan", "paged_decode",
                 "nvfp4kv_read_device_error", "nvfp4kv_status_string", "nvfp4kv_abi_version")
 
 
@@ -99,6 +99,9 @@ def lib():
         L.paged_prefill_causal.argtypes = [P, P, P, P, P, ctypes.POINTER(Cache), P, ctypes.c_float,
                                            ctypes.POINTER(PlanStruct), P, I64, P, P]
         L.paged_prefill_causal.restype = ctypes.c_int
+        L.paged_prefill_causal_noalloc.argtypes = [P, P, P, P, P, ctypes.POINTER(Cache), P, ctypes.c_float,
+                                                   ctypes.POINTER(PlanStruct), P, P]
+        L.paged_prefill_causal_noalloc.restype = ctypes.c_int
         L.nvfp4_decode_plan.argtypes = [P, I32, I32, I32, I32, I32, I32, ctypes.POINTER(DecodePlanStruct)]
         L.nvfp4_decode_plan.restype = ctypes.c_int
         L.paged_decode.argtypes = [P, P, P, P, ctypes.POINTER(Cache), P, ctypes.c_float,
@@ -381,6 +384,37 @@ def paged_prefill_causal(q: torch.Tensor, qo_indptr: torch.Tensor, kv_indptr: to
         _ptr(q), _ptr(qo_indptr), _ptr(kv_indptr), _ptr(page_table), _ptr(kv_lens), ctypes.byref(cs),
         _ptr(out), float(sm_scale), ctypes.byref(plan.struct), _ptr(ws),
         0 if ws is None else ws.numel(), _ptr(err), _stream(dev)), "paged_prefill_causal")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # NVFP4KV_NOALLOC_SCRATCH_BYTES
+
+
+def paged_prefill_causal_noalloc(q: torch.Tensor, qo_indptr: torch.Tensor, kv_indptr: torch.Tensor,
+                                 page_table: torch.Tensor, kv_lens: torch.Tensor, caches: PagedCache,
+                                 out: torch.Tensor, sm_scale: float, plan: Plan,
+                                 dev_error: torch.Tensor):
+    """paged_prefill_causal for callers that cannot allocate device memory:
+    every argument is already on the device (no plan is built, nothing is
+    uploaded, no workspace is requested) and the library takes its workspace
+    from its own per-GPU array.  Calls overlapping on one GPU race."""
+    dev = q.device
+    for name, t, dt in (("q", q, torch.bfloat16), ("out", out, torch.bfloat16),
+                        ("qo_indptr", qo_indptr, torch.int32), ("kv_indptr", kv_indptr, torch.int32),
+                        ("page_table", page_table, torch.int32), ("kv_lens", kv_lens, torch.int32),
+                        ("dev_error", dev_error, torch.int32)):
+        if t.dtype != dt or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor on {dev}")
+    if q.dim() != 3 or out.shape != q.shape or q.shape[2] != caches.head_dim:
+        raise ValueError("q/out must be [total_q, num_q_heads, head_dim]")
+    if q.shape[0] != plan.total_q or q.shape[1] != plan.num_q_heads:
+        raise ValueError("q does not match the plan")
+    _check_batch_arrays(plan, qo_indptr, kv_indptr, kv_lens, page_table)
+    cs = caches._struct()
+    _check(lib().paged_prefill_causal_noalloc(
+        _ptr(q), _ptr(qo_indptr), _ptr(kv_indptr), _ptr(page_table), _ptr(kv_lens), ctypes.byref(cs),
+        _ptr(out), float(sm_scale), ctypes.byref(plan.struct), _ptr(dev_error), _stream(dev)),
+        "paged_prefill_causal_noalloc")
     return out
 
 

@@ -31,7 +31,9 @@
 // of the S^T accumulators without any data movement.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "nvfp4kv_codec.hpp"
 #include "nvfp4kv_internal.hpp"
@@ -1189,3 +1191,51 @@ extern "C" int paged_prefill_causal(const void* q, const int32_t* qo_indptr,
 #undef NVFP4KV_CASE
   return hipGetLastError() == hipSuccess ? NVFP4KV_OK : NVFP4KV_EHIP;
 }
+
+// ---- paged_prefill_causal_noalloc: the same launch with the workspace taken
+// from a library-owned device array instead of the caller.  Each GPU holds its
+// own copy of the array (in the code object's device memory) until the
+// process ends; the host reaches it through the address that
+// hipGetSymbolAddress returns on that device, never through the array's name
+// (a host-side stand-in).
+namespace nvfp4kv {
+namespace {
+constexpr int64_t kNoallocScratchBytes = NVFP4KV_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+// The array's device address on the current device: looked up once per
+// device (with that device current), then reused.  Null if the lookup fails.
+void* scratch_device_ptr() {
+  static std::mutex mu;
+  static std::vector<void*> ptrs;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)ptrs.size() <= dev) ptrs.resize(dev + 1, nullptr);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
+}  // namespace
+}  // namespace nvfp4kv
+
+extern "C" int paged_prefill_causal_noalloc(const void* q, const int32_t* qo_indptr,
+                                            const int32_t* kv_indptr, const int32_t* page_table,
+                                            const int32_t* kv_lens, const nvfp4kv_cache* caches,
+                                            void* out, float sm_scale,
+                                            const nvfp4kv_prefill_plan* plan, uint32_t* dev_error,
+                                            void* stream) {
+  if (!plan) return NVFP4KV_EINVAL;
+  if (plan->workspace_bytes > kNoallocScratchBytes) return NVFP4KV_EWORKSPACE;
+  void* ws = nullptr;
+  if (plan->workspace_bytes > 0) {
+    ws = scratch_device_ptr();
+    if (!ws) return NVFP4KV_EHIP;
+  }
+  return paged_prefill_causal(q, qo_indptr, kv_indptr, page_table, kv_lens, caches, out, sm_scale,
+                              plan, ws, ws ? kNoallocScratchBytes : 0, dev_error, stream);
+}
+
