@@ -144,11 +144,20 @@ typedef struct {
           hardware conversion;
        3  as 0 with a bf16 staging tile, bf16 queries and probabilities and
           bf16 matrix instructions (0 stages f16: exact as well, fewer
-          instructions).
-     1 to 3 exist for head_dim 128, GQA group 4, 4-wave tiles (block_q 32)
+          instructions);
+       4  native low-precision scores ([PR #4769] code analysis: the branch
+          for matrix cores that take E2M1 operands): K requantized while
+          staged from NVFP4 (E4M3 scale per 16) to MXFP4 (E8M0 scale per
+          32, the format gfx950's scaled matrix instruction takes), queries
+          in MXFP8, S = Q K^T on the scaled FP4 x FP8 instruction; V and P
+          as 0.  Both requantizations round, so mode 4 has its own accuracy
+          contract: |o - o_ref| <= 0.75 (1 + |o_ref|) per element and
+          rms(o - o_ref) <= 0.2 rms(o_ref) per batch on N(0,1) data (its
+          typical per-row relative error is about 12%).
+     1 to 4 exist for head_dim 128, GQA group 4, 4-wave tiles (block_q 32)
      and page sizes dividing 64; other shapes return NVFP4KV_EUNSUPPORTED.
-     All give results within the same tolerance of the oracle (0, 1 and 2
-     bit-identical). */
+     0 to 3 give results within the same tolerance of the oracle (0, 1 and
+     2 bit-identical). */
   int32_t dequant_mode;
   int32_t cu_count;         /* CUs the tile width and the KV split were sized for */
   /* Order in which the Q tiles (or their KV chunks) are issued.  The plan

@@ -113,11 +113,11 @@ constexpr float kRescaleSlack = 8.0f;
 // ulp of m is no longer small and exp2 would overflow; such rows use the
 // exact form p = exp2((s - m) c) with m in raw score units.  A row may take
 // the exact form when c times the largest possible raw score (head_dim x
-// 2^15 x 2688: a query rescaled below 2^15 times the largest staged key,
-// 6 x 448) reaches 2^24.
-template <int D>
+// 2^15 x the largest key: a query rescaled below 2^15 times 6 x 448 staged,
+// or 6 x 512 requantized to MXFP4) reaches 2^24.
+template <int D, int DQ>
 __device__ __forceinline__ bool exact_scores(float c) {
-  constexpr float kMaxRaw = (float)D * 32768.0f * 2688.0f;
+  constexpr float kMaxRaw = (float)D * 32768.0f * (DQ == 4 ? 3072.0f : 2688.0f);
   return c * kMaxRaw >= 16777216.0f;
 }
 
@@ -184,7 +184,13 @@ __device__ __forceinline__ void static_for(F&& f) {
 //  2: as 0, with a byte-table decode of the codes instead of the hardware
 //     conversion;
 //  3: as 0, with a bf16 staging tile, bf16 queries and probabilities and the
-//     bf16 matrix instructions (the kernel's own 16-bit format is f16).
+//     bf16 matrix instructions (the kernel's own 16-bit format is f16);
+//  4: native low-precision scores in the OCP MX formats that gfx950's scaled
+//     matrix instruction consumes: K requantized from NVFP4 (E4M3 scale per
+//     16) to MXFP4 (E8M0 scale per 32) while it is staged, the queries in
+//     MXFP8, S^T = K Q^T on v_mfma_scale_f32_32x32x64_f8f6f4; V, P and O^T
+//     as in 0.  Both requantizations round, so this mode is held to a looser
+//     accuracy contract than the others.
 // The 16-bit operands travel as raw bits in f16x8 registers either way.
 // Eight codes (one dword) times the f16 scale pair SS, as four f16 pairs.
 // The 32x32x16 matrix instruction on 16-bit operands: f16, or bf16 for the
@@ -235,6 +241,105 @@ __device__ __forceinline__ u32x4 decode8(uint32_t x, f16x2 SS) {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// ---- dequant mode 4 (MX scores).  Operand layout of the scaled 32x32x64
+// FP4 x FP8 product (pinned on the device by the probe tests): an A lane
+// (row m = lane % 32, half h = lane / 32) holds two 16-element chunks of its
+// row, at contraction offsets 16h and 32 + 16h; a B lane (column n, half h)
+// holds the 32 consecutive contraction elements at 32h.  The scales follow
+// the A layout: the product of contraction element k takes the E8M0 byte of
+// A lane (m, g) and of B lane (n, g), g = (k / 16) % 2.  So both operands'
+// MX blocks are the 16-element chunks {g, g + 2} of a K-step: for K-step c
+// (head_dim 64c .. 64c + 63) the NVFP4 blocks 4c + g and 4c + 2 + g, MX
+// block (c, g).  A staged K row holds, for every (c, g), the pair's 16 code
+// bytes at 32c + 16g (block b at code_off(b)), then the E8M0 byte of (c, g)
+// at D/2 + 4g + c.
+template <int D>
+struct Mx {
+  static constexpr int KROW = D / 2 + 16;  // 16-byte aligned rows, 5 x 16 B for D = 128
+  __device__ static constexpr int code_off(int b) { return 32 * (b / 4) + 16 * (b % 2) + 8 * ((b / 2) % 2); }
+};
+
+// The E8M0 exponent of an MX block whose NVFP4 block scales are at most smax
+// (> 0, an E4M3 value, so a normal float): the smallest e with smax <= 2^e,
+// so that every requantized magnitude e2m1 x S_b / 2^e stays within E2M1's
+// range.
+__device__ __forceinline__ int mx_exponent_of_scale(float smax) {
+  const uint32_t b = f2u(smax);
+  return (int)(b >> 23) - 127 + ((b & 0x7FFFFFu) != 0u);
+}
+
+// MXFP8 query fragments: lane (row, half hh) holds for K-step c the 32
+// elements q[64c + 32hh .. +31] as E4M3 bytes (q8[c], 8 dwords): 16-element
+// chunks 2hh (MX block g = 0) and 2hh + 1 (g = 1) of the K-step.  The row is
+// first rescaled by 2^-sh exactly as the f16 path does (largest magnitude to
+// [2^14, 2^15)), so raw scores keep the same bound; then each MX block (the
+// chunks {g, g + 2}: half in each lane of the pair) takes the smallest E8M0
+// exponent e >= -127 with its largest magnitude a <= 448 x 2^e (nothing
+// saturates), and its elements are rounded to nearest-even E4M3 after the
+// exact multiplication by 2^-e.  Byte c of the returned word is e + 127 of
+// block (c, hh), the one this lane's scale operand carries; sh goes into
+// *cmul as 2^sh.
+template <int D>
+__device__ __forceinline__ uint32_t load_q_mx(const uint16_t* qrow, int hh, i32x8 (&q8)[D / 64], float& cmul) {
+  constexpr int NC = D / 64;
+  u32x4 qw[NC][4];
+  uint32_t bm[NC][2];  // largest |bf16| bit pattern of each MX block (t: chunk 2hh + t, block t)
+  uint32_t am = 0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      bm[c][t] = 0;
+#pragma unroll
+      for (int k = 2 * t; k < 2 * t + 2; ++k) {
+        qw[c][k] = *(const u32x4*)(qrow + 64 * c + 32 * hh + 8 * k);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          bm[c][t] = max(bm[c][t], max(qw[c][k][e] & 0x7FFFu, (qw[c][k][e] >> 16) & 0x7FFFu));
+      }
+      // the block's other chunk is in the partner lane (other half)
+      bm[c][t] = max(bm[c][t], (uint32_t)__shfl_xor((int)bm[c][t], 32));
+      am = max(am, bm[c][t]);
+    }
+  }
+  const int sh = am >= 0x80u ? min(max((int)(am >> 7) - 127 - 14, -100), 113) : 0;
+  const float down = u2f((uint32_t)(127 - sh) << 23);  // 2^-sh
+  cmul = u2f((uint32_t)(127 + sh) << 23);
+  uint32_t scales = 0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      // the block's largest magnitude after the row rescale (exact: 8 significant bits)
+      const uint32_t ab = f2u(u2f(bm[c][t] << 16) * down);
+      const int E = (int)(ab >> 23) - 127;
+      // 448 = 1.75 x 2^8: a <= 448 x 2^e  <=>  e >= E - 8 (+1 when a's significand exceeds 1.75)
+      const int e = ab < 0x00800000u ? -127 : max(E - 8 + ((ab & 0x7FFFFFu) > 0x600000u), -127);
+      if (t == hh) scales |= (uint32_t)(e + 127) << (8 * c);
+      // q x 2^-(sh + e) in two exact power-of-two steps (sh + e spans
+      // [-227, 120], beyond one float factor; a product that underflows in
+      // the first step is far below E4M3's smallest subnormal either way)
+      const int x = sh + e, x1 = x / 2;
+      const float f1 = u2f((uint32_t)(127 - x1) << 23), f2 = u2f((uint32_t)(127 - (x - x1)) << 23);
+      auto y = [&](uint32_t bits) { return (u2f(bits) * f1) * f2; };
+#pragma unroll
+      for (int k = 2 * t; k < 2 * t + 2; ++k)
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2) {
+          const uint32_t w0 = qw[c][k][2 * d2], w1 = qw[c][k][2 * d2 + 1];
+          s16x2 o = {};
+          o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, y(w0 << 16), y(w0 & 0xFFFF0000u), 1.0f, false);
+          o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, y(w1 << 16), y(w1 & 0xFFFF0000u), 1.0f, true);
+          q8[c][2 * k + d2] = __builtin_bit_cast(int, o);
+        }
+    }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) asm volatile("" ::"v"(q8[c]));
+  return scales;
+}
 
 // gfx950 LDS transpose read (ds_read_b64_tr_b16): within each group of 16
 // lanes, lane i receives elements i, 16+i, 32+i, 48+i of the 64 16-bit values
@@ -372,6 +477,9 @@ struct TileStager {
   uint32_t sw[C::JOBS_PER_THREAD];   // the part's two raw scale bytes
   uint8_t* sfp;                      // (DQ 1) where the K part's scale bytes go
   u32x4 chunk;
+  uint32_t R01;                      // (DQ 4) the K part's S_b / 2^e as an f16 pair (exact)
+  int kpart;                         // (DQ 4) the K part
+  uint2 kout;                        // (DQ 4) one requantized 16-element block
   __device__ __forceinline__ TileStager(const RawJob<D>* job, bool live, uint8_t* smem, int tid) {
 #pragma unroll
     for (int j = 0; j < C::JOBS_PER_THREAD; ++j) {
@@ -380,19 +488,62 @@ struct TileStager {
       const int rem = id - tensor * C::BN * C::PARTS;
       const int key = rem / C::PARTS, part = rem % C::PARTS;
       rowp[j] = tensor ? smem + C::K_STAGE + key * C::VROW + part * 64
-                       : (DQ == 1 ? smem + key * C::KRAW + part * 16 : smem + key * C::KROW + part * 64);
+                       : DQ == 1 ? smem + key * C::KRAW + part * 16
+                       : DQ == 4 ? smem + key * Mx<D>::KROW
+                                 : smem + key * C::KROW + part * 64;
       if (j == 0) sfp = smem + key * C::KRAW + 64 + 2 * part;
       // both E4M3 scales of the part in one conversion (dead keys: zero scales)
       sw[j] = live ? (scale_word<D>(job[j], part) >> (16 * (part & 1))) & 0xFFFFu : 0u;
       const f32x2 S = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw[j], 1.0f, false);
       const f16x2 Sh = {(_Float16)S[0], (_Float16)S[1]};
       S01[j] = __builtin_bit_cast(uint32_t, Sh);
+      if constexpr (DQ == 4) {
+        if (j == 0) {
+          // The part's blocks 2p + k (k = 0, 1) pair with blocks 2(p^1) + k
+          // of the neighbouring part into MX blocks (p/2, k); both parts
+          // compute the pair's exponent, the even one stores it.
+          kpart = part;
+          const uint32_t pw = live ? (scale_word<D>(job[0], part ^ 1) >> (16 * ((part ^ 1) & 1))) & 0xFFFFu : 0u;
+          const f32x2 Sp = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(pw, 1.0f, false);
+          uint32_t xb = 0;
+          f16x2 R;
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const float smax = __builtin_fmaxf(S[k], Sp[k]);
+            const int e = smax > 0.0f ? mx_exponent_of_scale(smax) : 0;
+            // S_b / 2^e: in (0, 1], 4 significant bits, at least 2^-18: exact in f16
+            R[k] = (_Float16)(S[k] * u2f((uint32_t)(127 - e) << 23));
+            xb |= (smax > 0.0f ? (uint32_t)(e + 127) : 0u) << (8 * k);
+          }
+          R01 = __builtin_bit_cast(uint32_t, R);
+          if ((part & 1) == 0) {
+            rowp[0][D / 2 + part / 2] = (uint8_t)(xb & 0xFFu);
+            rowp[0][D / 2 + 4 + part / 2] = (uint8_t)(xb >> 8);
+          }
+        }
+      }
     }
   }
   template <int P>
   __device__ __forceinline__ void piece(const RawJob<D>* job) {
     constexpr int j = P / 8, w = (P / 2) % 4, h = P % 2;
-    if constexpr (DQ == 1 && j == 0) {
+    if constexpr (DQ == 4 && j == 0) {
+      // requantize 4 codes of block 2p + w/2: e2m1(code) x S_b / 2^e (an
+      // exact f16 product, magnitude <= 6), rounded to nearest-even E2M1
+      static_assert(C::JOBS_PER_THREAD == 2, "MX scores: 4-wave tiles");
+      const _Float16 r = __builtin_bit_cast(f16x2, R01)[w / 2];
+      const f16x2 rr = {r, r};
+      const uint32_t x = job[0].pk[w];
+      uint32_t& out = w % 2 ? kout.y : kout.x;
+      if constexpr (h == 0) out = 0;
+      static_for<2 * h, 2 * h + 2>([&](auto bc) {
+        constexpr int sel = decltype(bc)::value;  // byte of the code word: elements 2 sel, 2 sel + 1
+        const f16x2 v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, sel) * rr;
+        out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f16(out, v, 1.0f, sel);
+      });
+      // the block's 8 code bytes (words 2k, 2k + 1 of the part) to their place
+      if constexpr (w % 2 == 1 && h == 1) *(uint2*)(rowp[0] + Mx<D>::code_off(2 * kpart + w / 2)) = kout;
+    } else if constexpr (DQ == 1 && j == 0) {
       // raw K: the part's 16 code bytes and its 2 scale bytes (job 0 is K
       // for 4-wave tiles, the only ones the ablation is built for)
       static_assert(C::JOBS_PER_THREAD == 2, "in-loop decode ablation: 4-wave tiles");
@@ -647,9 +798,18 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   const float gk = *a.kscale, gv = *a.vscale;
   if (tile == 0 && tid == 0 && !(scale_ok(gk) && scale_ok(gv)))
     atomicOr(a.err, (uint32_t)NVFP4KV_DEV_BAD_SCALE_ATTN);
-  f16x8 qf[C::NDC];
-  const float cscale = load_q<D, DQ>(a.q + ((int64_t)(q_begin + (row_valid ? tok : q0)) * a.Hq + hq) * D, hh,
-                                     a.sm_scale_log2 * gk, qf);
+  const uint16_t* const qrow = a.q + ((int64_t)(q_begin + (row_valid ? tok : q0)) * a.Hq + hq) * D;
+  f16x8 qf[C::NDC];    // 16-bit Q^T fragments (modes 0-3)
+  i32x8 q8[D / 64];    // MXFP8 Q^T fragments (mode 4)
+  uint32_t qsc = 0;    // their E8M0 scale bytes, one per K-step
+  float cscale;
+  if constexpr (DQ == 4) {
+    float cmul;
+    qsc = load_q_mx<D>(qrow, hh, q8, cmul);
+    cscale = a.sm_scale_log2 * gk * cmul;
+  } else {
+    cscale = load_q<D, DQ>(qrow, hh, a.sm_scale_log2 * gk, qf);
+  }
 
   f32x16 o[C::NDB];
 #pragma unroll
@@ -657,7 +817,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   // reference max: log2 units, or raw score units on a wave whose rows need
   // the exact score form (the same on every chunk of a split tile)
   float m_run = -__builtin_inff(), l_run = 0.0f;
-  const bool exact = __any(exact_scores<D>(cscale));
+  const bool exact = __any(exact_scores<D, DQ>(cscale));
 
   // V^T operand addressing (transpose reads): lane t of each 16-lane group
   // points at 4 consecutive head_dim values of one key.
@@ -691,9 +851,41 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     // and the staging of tile j+1 into the other buffer (then the loads of
     // tile j+2) is placed piece by piece between them, so that it issues
     // while the matrix core runs.  Scheduling barriers keep that order.
-    constexpr int NQK = 2 * C::NDC, KA = 3;
     f32x16 s[2];
     s[0] = s[1] = (f32x16){};
+    if constexpr (DQ == 4) {
+      // MX scores: the instruction (kb, c) = (i & 1, i >> 1) multiplies the
+      // MXFP4 keys of block kb by the MXFP8 queries of K-step c; the lane
+      // reads its 16 code bytes of each (kb, c) and one word of E8M0 bytes
+      // per kb (byte c: K-step c) up front.
+      constexpr int NQK = D / 32;
+      i32x8 kf[NQK];
+      uint32_t ksc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint8_t* row = sK + (kb * 32 + n) * Mx<D>::KROW;
+        ksc[kb] = *(const uint32_t*)(row + D / 2 + 4 * hh);
+#pragma unroll
+        for (int c = 0; c < D / 64; ++c) {
+          const u32x4 v = *(const u32x4*)(row + 32 * c + 16 * hh);
+          kf[2 * c + kb] = (i32x8){(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        }
+      }
+      TileStager<D, G, W, DQ> stager(job, live, smem + ((jt + 1) & 1) * STG, tid);
+      static_for<0, NQK>([&](auto ic) {
+        constexpr int i = decltype(ic)::value, kb = i & 1, c = i >> 1;
+        s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[i], q8[c], s[kb], 4, 0, c, ksc[kb], c, qsc);
+        constexpr int HP = TileStager<D, G, W, DQ>::PIECES;
+        constexpr int P0 = (i * HP + NQK - 1) / NQK, P1 = ((i + 1) * HP + NQK - 1) / NQK;
+        static_for<P0, P1>([&](auto pc) { stager.template piece<decltype(pc)::value>(job); });
+        if constexpr (i == NQK - 1) {
+          live = ka.load(a, job, jt + 2, page_next, page_bad);
+          page_next = ka.lookup(a, jt + 3);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    } else {
+    constexpr int NQK = 2 * C::NDC, KA = 3;
     f16x8 kf[KA];
     auto kread = [&](int i) {
       if constexpr (DQ == 1) {
@@ -729,6 +921,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     });
+    }
 
     // ---- causal mask (diagonal tiles only): key > kend  <=>  offset(i) > lim
     if constexpr (MASK) {
@@ -1172,14 +1365,16 @@ extern "C" int paged_prefill_causal(const void* q, const int32_t* qo_indptr,
     // dequant-placement ablation: head_dim 128, GQA group 4, 4-wave tiles,
     // page sizes dividing the KV tile
     if (D != 128 || G != 4 || W != 4 || kBlockN % c.page_size != 0 || p.dequant_mode < 1 ||
-        p.dequant_mode > 3)
+        p.dequant_mode > 4)
       return NVFP4KV_EUNSUPPORTED;
     if (p.dequant_mode == 1)
       hipLaunchKernelGGL((prefill_kernel<128, 4, 4, true, 1>), dim3(a.num_items), dim3(256), 0, s, a);
     else if (p.dequant_mode == 2)
       hipLaunchKernelGGL((prefill_kernel<128, 4, 4, true, 2>), dim3(a.num_items), dim3(256), 0, s, a);
-    else
+    else if (p.dequant_mode == 3)
       hipLaunchKernelGGL((prefill_kernel<128, 4, 4, true, 3>), dim3(a.num_items), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<128, 4, 4, true, 4>), dim3(a.num_items), dim3(256), 0, s, a);
     return hipGetLastError() == hipSuccess ? NVFP4KV_OK : NVFP4KV_EHIP;
   }
 #define NVFP4KV_CASE(DD, GG, WW) \

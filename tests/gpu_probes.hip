@@ -5,7 +5,9 @@
 //    nvfp4kv_codec.hpp, and records where the code changes;
 //  * MFMA lane layouts of v_mfma_f32_32x32x16_bf16 / 16x16x32_bf16;
 //  * the FP4 -> bf16 / fp32 hardware conversions with a scale operand;
-//  * the E4M3 (fp8) -> fp32 pair conversion used to decode block scales.
+//  * the E4M3 (fp8) -> fp32 pair conversion used to decode block scales;
+//  * the conversions and the scaled FP4 x FP8 matrix instruction of the MX
+//    score variant (f32 -> E4M3 pairs, f16 pairs -> E2M1).
 #include <hip/hip_runtime.h>
 #include "../nvfp4_paged_kv_amd/csrc/nvfp4kv_codec.hpp"
 
@@ -113,6 +115,62 @@ __global__ void fp8_pairs_kernel(float* out) {
   out[4 * t + 3] = hi.y;  // byte b0
 }
 
+// The scaled FP4 x FP8 product v_mfma_scale_f32_32x32x64_f8f6f4 (A in E2M1,
+// B in E4M3, one E8M0 scale per lane for A and for B, byte 0 of its scale
+// word): one wave, the register contents as given (a: 8 dwords per lane,
+// the first 4 used for FP4; b: 8 dwords per lane; sa, sb: one word per
+// lane); d: the 16 result registers of each lane.
+typedef int v8i __attribute__((ext_vector_type(8)));
+__global__ void mfma_scale_kernel(const int* a, const int* b, const int* sa, const int* sb, float* d) {
+  const int l = threadIdx.x;
+  v8i av, bv;
+  for (int j = 0; j < 8; ++j) {
+    av[j] = a[l * 8 + j];
+    bv[j] = b[l * 8 + j];
+  }
+  const int xa = sa[l], xb = sb[l];
+  f32x16 c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, (f32x16){}, 4, 0, 0, xa, 0, xb);
+  // the sources stay live until after the instruction, so that its result
+  // registers cannot overlap them
+  asm volatile("" : "+v"(c) : "v"(av), "v"(bv), "v"(xa), "v"(xb));
+  for (int r = 0; r < 16; ++r) d[l * 16 + r] = c[r];
+}
+
+// Every bf16 pattern through the f32 -> E4M3 pair conversion the MXFP8 query
+// load uses: thread t converts patterns 4t .. 4t+3 (as f32) into the bytes
+// 0 .. 3 of one word (two conversions, word select 0 then 1).
+__global__ void fp8_from_bf16_kernel(uint32_t* out) {
+  const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= 16384u) return;
+  typedef short s2 __attribute__((ext_vector_type(2)));
+  float v[4];
+  for (int i = 0; i < 4; ++i) v[i] = u2f((4u * t + (uint32_t)i) << 16);
+  s2 o = {};
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, v[0], v[1], 1.0f, false);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, v[2], v[3], 1.0f, true);
+  out[t] = __builtin_bit_cast(uint32_t, o);
+}
+
+// Every f16 pattern through the f16 pair -> E2M1 conversion the K
+// requantization uses: thread t converts patterns 8t .. 8t+7 into the
+// nibbles 0 .. 7 of one word (pair j into byte j).
+__global__ void fp4_from_f16_kernel(uint32_t* out) {
+  const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= 8192u) return;
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  h2 v[4];
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t bits = (8u * t + 2u * j) | ((8u * t + 2u * j + 1u) << 16);
+    v[j] = __builtin_bit_cast(h2, bits);
+  }
+  uint32_t o = 0;
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f16(o, v[0], 1.0f, 0);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f16(o, v[1], 1.0f, 1);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f16(o, v[2], 1.0f, 2);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f16(o, v[3], 1.0f, 3);
+  out[t] = o;
+}
+
 extern "C" {
 // All pointers are device pointers; every call synchronizes the device.
 int probe_e2m1_scan(uint32_t sign, int mode, uint32_t* count, uint32_t* buf, uint32_t cap) {
@@ -135,6 +193,18 @@ int probe_mfma32(const float* A, const float* B, float* D) {
 }
 int probe_fp8_pairs(float* out) {
   fp8_pairs_kernel<<<1, 128>>>(out);
+  return hipDeviceSynchronize() == hipSuccess ? 0 : -1;
+}
+int probe_fp8_from_bf16(uint32_t* out) {  // out: 16384 words
+  fp8_from_bf16_kernel<<<64, 256>>>(out);
+  return hipDeviceSynchronize() == hipSuccess ? 0 : -1;
+}
+int probe_fp4_from_f16(uint32_t* out) {  // out: 8192 words
+  fp4_from_f16_kernel<<<32, 256>>>(out);
+  return hipDeviceSynchronize() == hipSuccess ? 0 : -1;
+}
+int probe_mfma_scale(const int* a, const int* b, const int* sa, const int* sb, float* d) {
+  mfma_scale_kernel<<<1, 64>>>(a, b, sa, sb, d);
   return hipDeviceSynchronize() == hipSuccess ? 0 : -1;
 }
 int probe_mfma16(const float* A, const float* B, float* D) {

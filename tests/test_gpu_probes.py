@@ -2,7 +2,8 @@
 tests/libnvfp4kv_probes.so): the hardware FP4 conversion used by the append
 against the oracle's E2M1 encoder over every fp32 pattern, the FP4 -> fp32
 decode used by the attention's staging, the E4M3 pair decode of its block
-scales, and the MFMA lane layouts."""
+scales, the MFMA lane layouts, and what the MX score variant relies on: the
+scaled FP4 x FP8 matrix instruction and the two encoders that feed it."""
 import ctypes
 import os
 
@@ -23,7 +24,7 @@ def probes():
         pytest.fail("tests/libnvfp4kv_probes.so missing: run __graft_entry__.build()")
     L = ctypes.CDLL(path)
     for f in ("probe_e2m1_scan", "probe_cvt_pairs", "probe_fp4_to_bf16", "probe_mfma32", "probe_mfma16",
-              "probe_fp8_pairs"):
+              "probe_fp8_pairs", "probe_mfma_scale", "probe_fp8_from_bf16", "probe_fp4_from_f16"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -131,3 +132,92 @@ def test_mfma_16x16x32_layout(probes):
     Ad, Bd, Dd = A.cuda(), B.cuda(), torch.zeros(16, 16).cuda()
     assert probes.probe_mfma16(P(Ad), P(Bd), P(Dd)) == 0
     torch.testing.assert_close(Dd.cpu(), A.double().mm(B.double()).float(), rtol=1e-5, atol=1e-5)
+
+
+def test_mfma_scale_fp4_fp8_layout(probes, oracle):
+    """The scaled FP4 x FP8 32x32x64 product that the MX score variant uses
+    for S^T = K Q^T: lane l of A holds row l%32 with two 16-element chunks
+    (nibbles 0-15 and 16-31, the even element of a byte in its low nibble)
+    at contraction offsets 16(l//32) and 32 + 16(l//32); lane l of B holds
+    column l%32 with 32 consecutive contraction elements (byte j at offset
+    32(l//32) + j); the product of contraction element k takes the E8M0
+    scale (byte 0) of A lane m + 32g and of B lane n + 32g, g = (k//16)%2 --
+    the A layout's halves, not B's; the result has the 32x32 layout of the
+    16-bit products.  Random signed codes, random E4M3 bytes and a random
+    scale per lane, against the sum computed from the oracle's E2M1 and E4M3
+    decodes.  The instruction's own sum is not exact in fp32: it stays
+    within 2^-10 of the largest product (measured: 4.9e-4)."""
+    banner("scaled FP4 x FP8 matrix instruction layout")
+    rng = np.random.default_rng(7)
+    e2 = np.array([oracle.e2m1_value(c) for c in range(16)])
+    e4 = np.array([oracle.e4m3_value(c) for c in range(256)])
+    codes = rng.integers(0, 16, (64, 32))
+    fp8 = rng.integers(0, 256, (64, 32))
+    fp8[(fp8 & 0x7F) == 0x7F] = 0x38  # no NaN encodings
+    sa = rng.integers(120, 134, 64)
+    sb = rng.integers(120, 134, 64)
+    A = np.zeros((32, 64))
+    B = np.zeros((64, 32))
+    a_regs = np.zeros((64, 8), np.int64)
+    b_regs = np.zeros((64, 8), np.int64)
+    for l in range(64):
+        h = l // 32
+        for j in range(32):
+            k = (0 if j < 16 else 32) + 16 * h + j % 16
+            A[l % 32, k] = e2[codes[l, j]] * 2.0 ** (int(sa[l]) - 127)
+            a_regs[l, j // 8] |= int(codes[l, j]) << (4 * (j % 8))
+            kb = 32 * h + j
+            B[kb, l % 32] = e4[fp8[l, j]] * 2.0 ** (int(sb[l % 32 + 32 * ((kb // 16) % 2)]) - 127)
+            b_regs[l, j // 4] |= int(fp8[l, j]) << (8 * (j % 4))
+    # (device tensors held by name until the call returns: a temporary's
+    # memory could go to the next operand before the kernel reads it)
+    ta, tb, tsa, tsb = (torch.from_numpy((x & 0xFFFFFFFF).astype(np.uint32).view(np.int32)).cuda()
+                        for x in (a_regs, b_regs, sa, sb))
+    d = torch.zeros(64 * 16, dtype=torch.float32, device="cuda")
+    assert probes.probe_mfma_scale(P(ta), P(tb), P(tsa), P(tsb), P(d)) == 0
+    d = d.cpu().numpy().reshape(64, 16)
+    got = np.zeros((32, 32))
+    for l in range(64):
+        for r in range(16):
+            got[8 * (r // 4) + 4 * (l // 32) + r % 4, l % 32] = d[l, r]
+    ref = A @ B
+    largest = (np.abs(A)[:, :, None] * np.abs(B)[None, :, :]).max(axis=1)
+    assert (np.abs(got - ref) <= 2.0 ** -10 * largest).all(), np.max(np.abs(got - ref) / largest)
+
+
+def test_fp8_encode_of_every_bf16_matches_oracle(probes, oracle):
+    """The MXFP8 query load rounds bf16-valued floats of magnitude <= 448
+    (after an exact power-of-two scaling) with the pair conversion: every
+    bf16 pattern in that range, both word selects, against the oracle's
+    nearest-even E4M3 encoder with the sign bit on top."""
+    banner("f32 -> E4M3 pair conversion, every bf16 pattern")
+    out = torch.zeros(16384, dtype=torch.int32, device="cuda")
+    assert probes.probe_fp8_from_bf16(P(out)) == 0
+    got = out.cpu().numpy().view(np.uint32)
+    got = np.stack([(got >> (8 * i)) & 0xFF for i in range(4)], 1).reshape(-1)  # byte i: pattern 4t + i
+    pats = np.arange(65536, dtype=np.uint32)
+    v = (pats << 16).view(np.float32)
+    keep = np.isfinite(v) & (np.abs(v) <= 448.0)
+    got, v = got[keep], v[keep]
+    want = oracle.e4m3_encode(np.abs(v)).astype(np.uint32)
+    # magnitude codes equal; the sign bit too wherever the result is not zero
+    bad = np.nonzero(((got & 0x7F) != want) | ((want != 0) & ((got >> 7) != np.signbit(v))))[0]
+    assert bad.size == 0, [(float(v[i]), hex(int(got[i])), hex(int(want[i]))) for i in bad[:8]]
+
+
+def test_fp4_encode_of_every_f16_matches_oracle(probes, oracle):
+    """The K requantization rounds exact f16 products of magnitude <= 6 with
+    the f16 pair -> E2M1 conversion: every f16 pattern in that range, both
+    elements of each pair and all four byte selects, against the oracle's
+    nearest-even E2M1 encoder."""
+    banner("f16 pair -> E2M1 conversion, every f16 pattern")
+    out = torch.zeros(8192, dtype=torch.int32, device="cuda")
+    assert probes.probe_fp4_from_f16(P(out)) == 0
+    got = out.cpu().numpy().view(np.uint32)
+    got = np.stack([(got >> (4 * i)) & 0xF for i in range(8)], 1).reshape(-1)  # nibble i: pattern 8t + i
+    v = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float32)
+    keep = np.abs(v) <= 6.0
+    got, v = got[keep], v[keep]
+    want = oracle.e2m1_encode(v).astype(np.uint32)
+    bad = np.nonzero(((got & 7) != (want & 7)) | (((want & 7) != 0) & ((got >> 3) != (want >> 3))))[0]
+    assert bad.size == 0, [(float(v[i]), int(got[i]), int(want[i])) for i in bad[:8]]
