@@ -366,13 +366,14 @@ def bench_dequant_ablation(K, w, cache, dev_args, out, torch, per_graph=50, repl
     tiles decoded once per workgroup into f16 LDS (the kernel's own design), K
     decoded in registers inside the matrix loop, a byte-table decode, the
     f16 design with bf16 staging and bf16 matrix instructions instead, and
-    the native low-precision scores (K requantized to MXFP4 while staged, Q
-    in MXFP8, the scaled FP4 x FP8 matrix instruction; its own, looser
-    accuracy contract)."""
+    the native low-precision scores (K requantized to MXFP4, or MXFP8,
+    while staged, Q in MXFP8, the scaled matrix instruction; looser accuracy
+    contracts of their own)."""
     flops = attention_flops(w.q_lens, w.kv_lens, w.num_q_heads, w.head_dim)
     res = {}
     for mode, name in ((0, "lds_once_per_tile"), (1, "k_in_loop_registers"), (2, "lds_byte_table"),
-                       (3, "lds_once_per_tile_bf16"), (4, "native_mx_scores")):
+                       (3, "lds_once_per_tile_bf16"), (4, "native_mx_scores_fp4_keys"),
+                       (5, "native_mx_scores_fp8_keys")):
         plan = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), w.num_q_heads,
                       w.num_kv_heads, w.head_dim, w.page_size, kv_indptr=torch.from_numpy(w.kv_indptr),
                       tile_waves=4, dequant_mode=mode)

@@ -153,8 +153,11 @@ typedef struct {
           as 0.  Both requantizations round, so mode 4 has its own accuracy
           contract: |o - o_ref| <= 0.75 (1 + |o_ref|) per element and
           rms(o - o_ref) <= 0.2 rms(o_ref) per batch on N(0,1) data (its
-          typical per-row relative error is about 12%).
-     1 to 4 exist for head_dim 128, GQA group 4, 4-wave tiles (block_q 32)
+          typical per-row relative error is about 12%);
+       5  as 4 with K requantized to MXFP8 (E4M3 elements): twice the
+          staged K bytes, the same instruction rate, contract 0.3 and 0.05
+          (typical per-row relative error about 3%).
+     1 to 5 exist for head_dim 128, GQA group 4, 4-wave tiles (block_q 32)
      and page sizes dividing 64; other shapes return NVFP4KV_EUNSUPPORTED.
      0 to 3 give results within the same tolerance of the oracle (0, 1 and
      2 bit-identical). */

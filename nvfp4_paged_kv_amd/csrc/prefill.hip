@@ -114,10 +114,10 @@ constexpr float kRescaleSlack = 8.0f;
 // exact form p = exp2((s - m) c) with m in raw score units.  A row may take
 // the exact form when c times the largest possible raw score (head_dim x
 // 2^15 x the largest key: a query rescaled below 2^15 times 6 x 448 staged,
-// or 6 x 512 requantized to MXFP4) reaches 2^24.
+// or at most 6 x 512 requantized to MXFP4 or MXFP8) reaches 2^24.
 template <int D, int DQ>
 __device__ __forceinline__ bool exact_scores(float c) {
-  constexpr float kMaxRaw = (float)D * 32768.0f * (DQ == 4 ? 3072.0f : 2688.0f);
+  constexpr float kMaxRaw = (float)D * 32768.0f * (DQ >= 4 ? 3072.0f : 2688.0f);
   return c * kMaxRaw >= 16777216.0f;
 }
 
@@ -190,7 +190,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 //     16) to MXFP4 (E8M0 scale per 32) while it is staged, the queries in
 //     MXFP8, S^T = K Q^T on v_mfma_scale_f32_32x32x64_f8f6f4; V, P and O^T
 //     as in 0.  Both requantizations round, so this mode is held to a looser
-//     accuracy contract than the others.
+//     accuracy contract than the others;
+//  5: as 4 with K requantized to MXFP8 (E4M3 elements) instead: twice the
+//     staged K bytes of 4, the same instruction rate (the FP8 queries set
+//     it), a much smaller requantization error.
 // The 16-bit operands travel as raw bits in f16x8 registers either way.
 // Eight codes (one dword) times the f16 scale pair SS, as four f16 pairs.
 // The 32x32x16 matrix instruction on 16-bit operands: f16, or bf16 for the
@@ -244,22 +247,28 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
-// ---- dequant mode 4 (MX scores).  Operand layout of the scaled 32x32x64
-// FP4 x FP8 product (pinned on the device by the probe tests): an A lane
+// ---- dequant modes 4 and 5 (MX scores).  Operand layout of the scaled
+// 32x32x64 product (pinned on the device by the probe tests): an FP4 A lane
 // (row m = lane % 32, half h = lane / 32) holds two 16-element chunks of its
-// row, at contraction offsets 16h and 32 + 16h; a B lane (column n, half h)
-// holds the 32 consecutive contraction elements at 32h.  The scales follow
-// the A layout: the product of contraction element k takes the E8M0 byte of
-// A lane (m, g) and of B lane (n, g), g = (k / 16) % 2.  So both operands'
-// MX blocks are the 16-element chunks {g, g + 2} of a K-step: for K-step c
-// (head_dim 64c .. 64c + 63) the NVFP4 blocks 4c + g and 4c + 2 + g, MX
-// block (c, g).  A staged K row holds, for every (c, g), the pair's 16 code
-// bytes at 32c + 16g (block b at code_off(b)), then the E8M0 byte of (c, g)
-// at D/2 + 4g + c.
-template <int D>
+// row, at contraction offsets 16h and 32 + 16h; an FP8 A lane, and every B
+// lane (column n, half h), holds the 32 consecutive contraction elements at
+// 32h.  The scales do not follow the FP8 layout: for either format the
+// product of contraction element k takes the E8M0 byte of A lane (m, g) and
+// of B lane (n, g), g = (k / 16) % 2.  So both operands' MX blocks are the
+// 16-element chunks {g, g + 2} of a K-step: for K-step c (head_dim 64c ..
+// 64c + 63) the NVFP4 blocks 4c + g and 4c + 2 + g, MX block (c, g).  A
+// staged K row holds the requantized elements (FP4: for every (c, g) the
+// pair's 16 code bytes at 32c + 16g; FP8: element d at byte d; block b at
+// code_off(b) either way), then the E8M0 byte of (c, g) at CODES + 4g + c.
+template <int D, int DQ>
 struct Mx {
-  static constexpr int KROW = D / 2 + 16;  // 16-byte aligned rows, 5 x 16 B for D = 128
-  __device__ static constexpr int code_off(int b) { return 32 * (b / 4) + 16 * (b % 2) + 8 * ((b / 2) % 2); }
+  static constexpr bool FP8 = DQ == 5;
+  static constexpr int CODES = FP8 ? D : D / 2;  // element bytes of a staged K row
+  static constexpr int KROW = CODES + 16;        // 16-byte aligned rows
+  static constexpr int FRAG = FP8 ? 32 : 16;     // A-operand bytes of one lane and K-step
+  __device__ static constexpr int code_off(int b) {
+    return FP8 ? 16 * b : 32 * (b / 4) + 16 * (b % 2) + 8 * ((b / 2) % 2);
+  }
 };
 
 // The E8M0 exponent of an MX block whose NVFP4 block scales are at most smax
@@ -269,6 +278,13 @@ struct Mx {
 __device__ __forceinline__ int mx_exponent_of_scale(float smax) {
   const uint32_t b = f2u(smax);
   return (int)(b >> 23) - 127 + ((b & 0x7FFFFFu) != 0u);
+}
+
+// The same for MXFP8 elements: the smallest e with 6 smax <= 448 x 2^e (6 smax
+// is exact in f32; 448 = 1.75 x 2^8).
+__device__ __forceinline__ int mx8_exponent_of_scale(float smax) {
+  const uint32_t b = f2u(6.0f * smax);
+  return (int)(b >> 23) - 127 - 8 + ((b & 0x7FFFFFu) > 0x600000u);
 }
 
 // MXFP8 query fragments: lane (row, half hh) holds for K-step c the 32
@@ -282,9 +298,10 @@ __device__ __forceinline__ int mx_exponent_of_scale(float smax) {
 // exact multiplication by 2^-e.  Byte c of the returned word is e + 127 of
 // block (c, hh), the one this lane's scale operand carries; sh goes into
 // *cmul as 2^sh.
-template <int D>
-__device__ __forceinline__ uint32_t load_q_mx(const uint16_t* qrow, int hh, i32x8 (&q8)[D / 64], float& cmul) {
-  constexpr int NC = D / 64;
+// (DQ only gives each kernel its own instance: the host pass of this compiler
+// rejects a second kernel's call to a shared instance of this function)
+template <int DQ, int NC>
+__device__ __forceinline__ uint32_t load_q_mx(const uint16_t* qrow, int hh, i32x8 (&q8)[NC], float& cmul) {
   u32x4 qw[NC][4];
   uint32_t bm[NC][2];  // largest |bf16| bit pattern of each MX block (t: chunk 2hh + t, block t)
   uint32_t am = 0;
@@ -477,9 +494,10 @@ struct TileStager {
   uint32_t sw[C::JOBS_PER_THREAD];   // the part's two raw scale bytes
   uint8_t* sfp;                      // (DQ 1) where the K part's scale bytes go
   u32x4 chunk;
-  uint32_t R01;                      // (DQ 4) the K part's S_b / 2^e as an f16 pair (exact)
-  int kpart;                         // (DQ 4) the K part
+  uint32_t R01;                      // (DQ 4, 5) the K part's S_b / 2^e as an f16 pair (exact)
+  int kpart;                         // (DQ 4, 5) the K part
   uint2 kout;                        // (DQ 4) one requantized 16-element block
+  u32x4 kout8;                       // (DQ 5) one requantized 16-element block
   __device__ __forceinline__ TileStager(const RawJob<D>* job, bool live, uint8_t* smem, int tid) {
 #pragma unroll
     for (int j = 0; j < C::JOBS_PER_THREAD; ++j) {
@@ -489,7 +507,7 @@ struct TileStager {
       const int key = rem / C::PARTS, part = rem % C::PARTS;
       rowp[j] = tensor ? smem + C::K_STAGE + key * C::VROW + part * 64
                        : DQ == 1 ? smem + key * C::KRAW + part * 16
-                       : DQ == 4 ? smem + key * Mx<D>::KROW
+                       : DQ >= 4 ? smem + key * Mx<D, DQ>::KROW
                                  : smem + key * C::KROW + part * 64;
       if (j == 0) sfp = smem + key * C::KRAW + 64 + 2 * part;
       // both E4M3 scales of the part in one conversion (dead keys: zero scales)
@@ -497,7 +515,7 @@ struct TileStager {
       const f32x2 S = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw[j], 1.0f, false);
       const f16x2 Sh = {(_Float16)S[0], (_Float16)S[1]};
       S01[j] = __builtin_bit_cast(uint32_t, Sh);
-      if constexpr (DQ == 4) {
+      if constexpr (DQ >= 4) {
         if (j == 0) {
           // The part's blocks 2p + k (k = 0, 1) pair with blocks 2(p^1) + k
           // of the neighbouring part into MX blocks (p/2, k); both parts
@@ -510,15 +528,16 @@ struct TileStager {
 #pragma unroll
           for (int k = 0; k < 2; ++k) {
             const float smax = __builtin_fmaxf(S[k], Sp[k]);
-            const int e = smax > 0.0f ? mx_exponent_of_scale(smax) : 0;
-            // S_b / 2^e: in (0, 1], 4 significant bits, at least 2^-18: exact in f16
+            const int e = smax > 0.0f ? (Mx<D, DQ>::FP8 ? mx8_exponent_of_scale(smax) : mx_exponent_of_scale(smax)) : 0;
+            // S_b / 2^e, 4 significant bits: FP4 in (0, 1] and at least
+            // 2^-18, FP8 in (0, 75) and at least 2^-12: exact in f16
             R[k] = (_Float16)(S[k] * u2f((uint32_t)(127 - e) << 23));
             xb |= (smax > 0.0f ? (uint32_t)(e + 127) : 0u) << (8 * k);
           }
           R01 = __builtin_bit_cast(uint32_t, R);
           if ((part & 1) == 0) {
-            rowp[0][D / 2 + part / 2] = (uint8_t)(xb & 0xFFu);
-            rowp[0][D / 2 + 4 + part / 2] = (uint8_t)(xb >> 8);
+            rowp[0][Mx<D, DQ>::CODES + part / 2] = (uint8_t)(xb & 0xFFu);
+            rowp[0][Mx<D, DQ>::CODES + 4 + part / 2] = (uint8_t)(xb >> 8);
           }
         }
       }
@@ -542,7 +561,23 @@ struct TileStager {
         out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f16(out, v, 1.0f, sel);
       });
       // the block's 8 code bytes (words 2k, 2k + 1 of the part) to their place
-      if constexpr (w % 2 == 1 && h == 1) *(uint2*)(rowp[0] + Mx<D>::code_off(2 * kpart + w / 2)) = kout;
+      if constexpr (w % 2 == 1 && h == 1) *(uint2*)(rowp[0] + Mx<D, DQ>::code_off(2 * kpart + w / 2)) = kout;
+    } else if constexpr (DQ == 5 && j == 0) {
+      // requantize 4 codes of block 2p + w/2: e2m1(code) x S_b / 2^e (an
+      // exact f16 product, magnitude <= 448), rounded to nearest-even E4M3,
+      // one byte per element in head_dim order
+      static_assert(C::JOBS_PER_THREAD == 2, "MX scores: 4-wave tiles");
+      const _Float16 r = __builtin_bit_cast(f16x2, R01)[w / 2];
+      const f16x2 rr = {r, r};
+      const uint32_t x = job[0].pk[w];
+      s16x2 o = {};
+      o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(o, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 2 * h) * rr,
+                                                   1.0f, false);
+      o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(o, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 2 * h + 1) * rr,
+                                                   1.0f, true);
+      kout8[2 * (w % 2) + h] = __builtin_bit_cast(uint32_t, o);
+      // the block's 16 element bytes (words 2k, 2k + 1 of the part) to their place
+      if constexpr (w % 2 == 1 && h == 1) *(u32x4*)(rowp[0] + Mx<D, DQ>::code_off(2 * kpart + w / 2)) = kout8;
     } else if constexpr (DQ == 1 && j == 0) {
       // raw K: the part's 16 code bytes and its 2 scale bytes (job 0 is K
       // for 4-wave tiles, the only ones the ablation is built for)
@@ -800,12 +835,12 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     atomicOr(a.err, (uint32_t)NVFP4KV_DEV_BAD_SCALE_ATTN);
   const uint16_t* const qrow = a.q + ((int64_t)(q_begin + (row_valid ? tok : q0)) * a.Hq + hq) * D;
   f16x8 qf[C::NDC];    // 16-bit Q^T fragments (modes 0-3)
-  i32x8 q8[D / 64];    // MXFP8 Q^T fragments (mode 4)
+  i32x8 q8[D / 64];    // MXFP8 Q^T fragments (modes 4, 5)
   uint32_t qsc = 0;    // their E8M0 scale bytes, one per K-step
   float cscale;
-  if constexpr (DQ == 4) {
+  if constexpr (DQ >= 4) {
     float cmul;
-    qsc = load_q_mx<D>(qrow, hh, q8, cmul);
+    qsc = load_q_mx<DQ>(qrow, hh, q8, cmul);
     cscale = a.sm_scale_log2 * gk * cmul;
   } else {
     cscale = load_q<D, DQ>(qrow, hh, a.sm_scale_log2 * gk, qf);
@@ -853,28 +888,31 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     // while the matrix core runs.  Scheduling barriers keep that order.
     f32x16 s[2];
     s[0] = s[1] = (f32x16){};
-    if constexpr (DQ == 4) {
+    if constexpr (DQ >= 4) {
       // MX scores: the instruction (kb, c) = (i & 1, i >> 1) multiplies the
-      // MXFP4 keys of block kb by the MXFP8 queries of K-step c; the lane
-      // reads its 16 code bytes of each (kb, c) and one word of E8M0 bytes
-      // per kb (byte c: K-step c) up front.
+      // MXFP4 (MXFP8) keys of block kb by the MXFP8 queries of K-step c; the
+      // lane reads its 16 (32) element bytes of each (kb, c) and one word of
+      // E8M0 bytes per kb (byte c: K-step c) up front.
+      using X = Mx<D, DQ>;
       constexpr int NQK = D / 32;
       i32x8 kf[NQK];
       uint32_t ksc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const uint8_t* row = sK + (kb * 32 + n) * Mx<D>::KROW;
-        ksc[kb] = *(const uint32_t*)(row + D / 2 + 4 * hh);
+        const uint8_t* row = sK + (kb * 32 + n) * X::KROW;
+        ksc[kb] = *(const uint32_t*)(row + X::CODES + 4 * hh);
 #pragma unroll
         for (int c = 0; c < D / 64; ++c) {
-          const u32x4 v = *(const u32x4*)(row + 32 * c + 16 * hh);
-          kf[2 * c + kb] = (i32x8){(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+          const uint8_t* f = row + 2 * X::FRAG * c + X::FRAG * hh;
+          const u32x4 v = *(const u32x4*)f;
+          const u32x4 v2 = X::FP8 ? *(const u32x4*)(f + 16) : (u32x4){0u, 0u, 0u, 0u};
+          kf[2 * c + kb] = (i32x8){(int)v[0], (int)v[1], (int)v[2], (int)v[3], (int)v2[0], (int)v2[1], (int)v2[2], (int)v2[3]};
         }
       }
       TileStager<D, G, W, DQ> stager(job, live, smem + ((jt + 1) & 1) * STG, tid);
       static_for<0, NQK>([&](auto ic) {
         constexpr int i = decltype(ic)::value, kb = i & 1, c = i >> 1;
-        s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[i], q8[c], s[kb], 4, 0, c, ksc[kb], c, qsc);
+        s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[i], q8[c], s[kb], X::FP8 ? 0 : 4, 0, c, ksc[kb], c, qsc);
         constexpr int HP = TileStager<D, G, W, DQ>::PIECES;
         constexpr int P0 = (i * HP + NQK - 1) / NQK, P1 = ((i + 1) * HP + NQK - 1) / NQK;
         static_for<P0, P1>([&](auto pc) { stager.template piece<decltype(pc)::value>(job); });
@@ -1365,7 +1403,7 @@ extern "C" int paged_prefill_causal(const void* q, const int32_t* qo_indptr,
     // dequant-placement ablation: head_dim 128, GQA group 4, 4-wave tiles,
     // page sizes dividing the KV tile
     if (D != 128 || G != 4 || W != 4 || kBlockN % c.page_size != 0 || p.dequant_mode < 1 ||
-        p.dequant_mode > 4)
+        p.dequant_mode > 5)
       return NVFP4KV_EUNSUPPORTED;
     if (p.dequant_mode == 1)
       hipLaunchKernelGGL((prefill_kernel<128, 4, 4, true, 1>), dim3(a.num_items), dim3(256), 0, s, a);
@@ -1373,8 +1411,10 @@ extern "C" int paged_prefill_causal(const void* q, const int32_t* qo_indptr,
       hipLaunchKernelGGL((prefill_kernel<128, 4, 4, true, 2>), dim3(a.num_items), dim3(256), 0, s, a);
     else if (p.dequant_mode == 3)
       hipLaunchKernelGGL((prefill_kernel<128, 4, 4, true, 3>), dim3(a.num_items), dim3(256), 0, s, a);
-    else
+    else if (p.dequant_mode == 4)
       hipLaunchKernelGGL((prefill_kernel<128, 4, 4, true, 4>), dim3(a.num_items), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<128, 4, 4, true, 5>), dim3(a.num_items), dim3(256), 0, s, a);
     return hipGetLastError() == hipSuccess ? NVFP4KV_OK : NVFP4KV_EHIP;
   }
 #define NVFP4KV_CASE(DD, GG, WW) \

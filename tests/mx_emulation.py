@@ -1,7 +1,7 @@
-"""fp64 emulation of the prefill's MX score variant (dequant mode 4), for the
-tests: what the kernel's scaled FP4 x FP8 matrix instruction is fed, rebuilt
-on the CPU from the oracle's encoders and tables, and the attention over those
-operands computed by the oracle itself.
+"""fp64 emulation of the prefill's MX score variants (dequant modes 4 and 5),
+for the tests: what the kernel's scaled matrix instruction is fed, rebuilt on
+the CPU from the oracle's encoders and tables, and the attention over those
+operands.
 
 The PR #4769 page ("NVFP4 KV tile repack", code-analysis section) has a
 branch for targets whose matrix cores take E2M1 operands natively.  gfx950's
@@ -23,23 +23,30 @@ exact path.  The recipe, as the kernel applies it:
   magnitude a <= 448 * 2^e, and its elements are rounded to nearest-even
   E4M3 after the exact division by 2^(sh + e): q_hat = E4M3 * 2^(sh + e).
   Nothing saturates.
-* keys (MXFP4): the NVFP4 blocks 4c + g and 4c + 2 + g of a row form MX
-  block (c, g), with e = ceil(log2 max(S_a, S_b)); every element e2m1 * S_b
-  becomes the nearest-even E2M1 value of e2m1 * S_b / 2^e, times 2^e (times
-  the global scale g_k).
+* keys, mode 4 (MXFP4): the NVFP4 blocks 4c + g and 4c + 2 + g of a row
+  form MX block (c, g), with e = ceil(log2 max(S_a, S_b)); every element
+  e2m1 * S_b becomes the nearest-even E2M1 value of e2m1 * S_b / 2^e, times
+  2^e (times the global scale g_k);
+* keys, mode 5 (MXFP8): the same blocks, with the smallest e such that
+  6 max(S_a, S_b) <= 448 * 2^e, and the elements rounded to nearest-even
+  E4M3 instead.
 
-The requantized keys are handed to the oracle as an NVFP4 cache with block
-scale 2^(e - 1) and global scale 2 g_k (an E4M3 scale cannot hold 2^9, which
-e reaches when S = 448), the requantized queries as bf16 (every E4M3 value
-times a power of two in range is a bf16 value); both conversions are checked
-to be exact.
+Mode 4: the requantized keys are handed to the oracle as an NVFP4 cache with
+block scale 2^(e - 1) and global scale 2 g_k (an E4M3 scale cannot hold 2^9,
+which e reaches when S = 448), the requantized queries as bf16 (every E4M3
+value times a power of two in range is a bf16 value); both conversions are
+checked to be exact.  Mode 5's keys are not NVFP4 values, so its attention is
+dense_prefill below: a direct fp64 transcription of the oracle's definition
+(pinned against the oracle on exact operands).
 """
 import numpy as np
 
-# The variant's accuracy contract against the oracle (the emulation reaches
-# 0.45 and 0.115 on N(0,1) workloads of the prefill's shapes):
-MX_ELEM = 0.75  # |out - ref| <= MX_ELEM * (1 + |ref|) per element
-MX_RMS = 0.2    # rms(out - ref) <= MX_RMS * rms(ref) over a batch
+# The variants' accuracy contracts against the oracle, per mode: (elem, rms)
+# with |out - ref| <= elem * (1 + |ref|) per element and rms(out - ref) <=
+# rms * rms(ref) over a batch.  On N(0,1) workloads of the prefill's shapes
+# the emulation reaches 0.45 / 0.115 (mode 4) and 0.185 / 0.032 (mode 5).
+MX_CONTRACT = {4: (0.75, 0.2), 5: (0.3, 0.05)}
+MX_ELEM, MX_RMS = MX_CONTRACT[4]
 
 
 def _tables(O):
@@ -131,6 +138,46 @@ def mx_key_rows(O, codes, sf):
     return new, e
 
 
+def mx8_key_values(O, codes, sf):
+    """Requantize NVFP4 rows to MXFP8 (mode 5): values [rows, D] (without the
+    global scale) and the MX exponent of each NVFP4 block [rows, D/16]."""
+    e2, e4 = _tables(O)
+    c = _unpack(codes)
+    rows, D = c.shape
+    S = e4[sf.astype(np.int64)]
+    smax = np.maximum(S, S[:, [mx_partner(b) for b in range(D // 16)]])
+    E, sig = _exponent(np.where(smax > 0, 6.0 * smax, 1.0))
+    e = np.where(smax > 0, E - 8 + (sig > 1.75), 0)
+    vals = e2[c] * np.repeat(S * np.exp2(-e.astype(np.float64)), 16, axis=1)
+    assert np.abs(vals).max() <= 448.0
+    codes8 = O.e4m3_encode(np.abs(vals).astype(np.float32).reshape(-1)).reshape(rows, D)
+    out = np.copysign(e4[codes8.astype(np.int64)], vals) * np.repeat(np.exp2(e.astype(np.float64)), 16, axis=1)
+    return out, e
+
+
+def dense_prefill(q, k_rows, v_rows, qo, kv_indptr, page_table, kv_lens, page_size, num_kv_heads, sm_scale):
+    """fp64 causal paged prefill over dense operands: q [total_q, H_q, D]
+    values, k_rows / v_rows [(slot * H_kv + head), D] values; the oracle's
+    definition (bottom-right causal alignment, query head h reads KV head
+    h / (H_q / H_kv), softmax(sm_scale q.k) v) written with numpy."""
+    total_q, Hq, D = q.shape
+    G = Hq // num_kv_heads
+    out = np.zeros((total_q, Hq, D))
+    for r in range(len(kv_lens)):
+        Lk = int(kv_lens[r])
+        q0, q1 = int(qo[r]), int(qo[r + 1])
+        Lq = q1 - q0
+        j = np.arange(Lk)
+        slots = page_table[kv_indptr[r] + j // page_size].astype(np.int64) * page_size + j % page_size
+        vis = np.arange(Lk)[None, :] <= (Lk - Lq + np.arange(Lq))[:, None]
+        for h in range(Hq):
+            rows = slots * num_kv_heads + h // G
+            sc = np.where(vis, (q[q0:q1, h] @ k_rows[rows].T) * sm_scale, -np.inf)
+            p = np.exp(sc - sc.max(axis=1, keepdims=True))
+            out[q0:q1, h] = (p @ v_rows[rows]) / p.sum(axis=1, keepdims=True)
+    return out
+
+
 def mx_key_cache(O, k_cache, k_sf, k_scale):
     """The requantized keys as an NVFP4 cache for the oracle: (codes, scale
     bytes, global scale) with values e2m1' * 2^(e - 1) * (2 g_k)."""
@@ -148,11 +195,11 @@ def mx_key_cache(O, k_cache, k_sf, k_scale):
     return _pack(new).reshape(shp_c), sfb.reshape(shp_s), g2
 
 
-def mx_outputs(O, w, reqs=None):
+def mx_outputs(O, w, reqs=None, mode=4):
     """The MX variant's fp64 output rows for `reqs` of workload w (all if
     None) and their row indices in w's query order: the oracle's append of
-    w's bf16 K and V, the requantized queries and keys, the oracle's
-    attention over them."""
+    w's bf16 K and V, the requantized queries and keys, the attention over
+    them (the oracle's for mode 4, dense_prefill for mode 5)."""
     from gpu_helpers import sub_workload
     if reqs is None:
         reqs = range(w.batch)
@@ -163,6 +210,14 @@ def mx_outputs(O, w, reqs=None):
     ksf = np.zeros((P, ps, H, D // 16), np.uint8)
     vsf = np.zeros_like(ksf)
     assert O.append(s["k"], s["v"], s["slots"], w.k_scale, w.v_scale, kc, vc, ksf, vsf, ps) == 0
+    if mode == 5:
+        q_hat, _ = mx_query_values(O, s["q"])
+        kv, _ = mx8_key_values(O, kc.reshape(-1, D // 2), ksf.reshape(-1, D // 16))
+        rows = np.arange(P * ps * H)
+        vv = O.dequant_rows(vc.reshape(-1, D // 2), vsf.reshape(-1, D // 16), rows, D, w.v_scale)
+        out = dense_prefill(q_hat, kv * np.float64(np.float32(w.k_scale)), vv, s["qo"], s["kv_indptr"],
+                            s["page_table"], s["kv_lens"], ps, H, w.sm_scale)
+        return out, s["q_rows"]
     kc2, ksf2, g2 = mx_key_cache(O, kc, ksf, w.k_scale)
     out, err = O.prefill(mx_query_bits(O, s["q"]), s["qo"], s["kv_indptr"], s["page_table"], s["kv_lens"],
                          kc2, vc, ksf2, vsf, g2, w.v_scale, w.num_q_heads, w.sm_scale)

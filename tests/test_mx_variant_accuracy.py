@@ -1,19 +1,22 @@
-"""The prefill's MX score variant (dequant mode 4) on the CPU: pins of its
-emulation (tests/mx_emulation.py) and the accuracy contract derived from it.
+"""The prefill's MX score variants (dequant modes 4 and 5) on the CPU: pins
+of their emulation (tests/mx_emulation.py) and the accuracy contracts derived
+from it.
 
 gfx950's scaled f8f6f4 matrix instruction takes FP4 / FP8 elements with one
 power-of-two (E8M0) scale per 32 elements; the cache holds E2M1 codes with an
 E4M3 scale per 16 (the PR #4769 page's NVFP4 tiles).  Mode 4 requantizes K to
-MXFP4 and Q to MXFP8, both of which round, so it cannot meet the exact path's
-1e-2 + 1e-2 |ref| bound.  Its contract, measured here on the emulation over
-N(0,1) workloads of the prefill's shapes and checked on the GPU against the
-oracle by tests/test_gpu_mx_scores.py:
+MXFP4, mode 5 to MXFP8, and both Q to MXFP8; all of these round, so neither
+meets the exact path's 1e-2 + 1e-2 |ref| bound.  Each mode's contract
+(mx_emulation.MX_CONTRACT[mode] = (elem, rms)), measured here on the
+emulation over N(0,1) workloads of the prefill's shapes and checked on the
+GPU against the oracle by tests/test_gpu_mx_scores.py:
 
-* per element: |out - ref| <= MX_ELEM * (1 + |ref|);
-* over a batch: rms(out - ref) <= MX_RMS * rms(ref).
+* per element: |out - ref| <= elem * (1 + |ref|);
+* over a batch: rms(out - ref) <= rms * rms(ref).
 
-The emulation reaches at most 0.45 and 0.115 on these workloads; the bounds
-leave a margin for other draws.  Everything here runs on the CPU.
+The emulation reaches at most 0.45 / 0.115 (mode 4) and 0.185 / 0.032
+(mode 5) on these workloads; the bounds leave a margin for other draws.
+Everything here runs on the CPU.
 """
 import numpy as np
 import pytest
@@ -132,9 +135,56 @@ def test_key_requantization_error_bound(oracle, tables):
     assert np.allclose(np.abs(np.abs(kq / unit) - np.abs(k / unit)), nearest)
 
 
-def _ratio_stats(O, w):
+def test_mx8_keys_exact_when_representable(oracle):
+    """MXFP8 keys: a pair with equal power-of-two scales keeps every value
+    (e2m1 x 2^k has at most 2 significant bits), and any value is within
+    half an E4M3 step (2^-4 relative, 2^-10 x 2^e absolute) of e2m1 x S."""
+    e2, e4 = M._tables(oracle)
+    rng = np.random.default_rng(6)
+    codes = _rows_of(rng, 64)
+    ex = rng.integers(-6, 9, (64, 4))
+    sf = np.zeros((64, 8), np.uint8)
+    for b in range(8):
+        sf[:, b] = ((ex[:, 2 * (b // 4) + b % 2] + 7) << 3).astype(np.uint8)
+    vals, _ = M.mx8_key_values(oracle, codes, sf)
+    exact = e2[M._unpack(codes)] * np.repeat(e4[sf.astype(np.int64)], 16, 1)
+    assert np.array_equal(vals, exact)
+    sf = rng.integers(1, 0x7F, (256, 8)).astype(np.uint8)
+    codes = _rows_of(rng, 256)
+    vals, e = M.mx8_key_values(oracle, codes, sf)
+    exact = e2[M._unpack(codes)] * np.repeat(e4[sf.astype(np.int64)], 16, 1)
+    unit = np.repeat(np.exp2(e.astype(np.float64)), 16, 1)
+    assert (np.abs(vals - exact) <= np.maximum(2.0 ** -4 * np.abs(exact), 2.0 ** -10 * unit)).all()
+    # the exponent is the smallest with 6 max(S_a, S_b) <= 448 x 2^e
+    S = e4[sf.astype(np.int64)]
+    bound = 6 * np.maximum(S, S[:, [b ^ 2 for b in range(8)]]) / np.exp2(e.astype(np.float64))
+    assert ((bound > 224) & (bound <= 448)).all()
+
+
+def test_dense_prefill_matches_the_oracle(oracle):
+    """dense_prefill (mode 5's attention) on the exact dequantized operands
+    equals the oracle's prefill to fp64 rounding."""
+    from gpu_helpers import sub_workload
+    w = W.make_attention("ragged_amax", RAGGED_Q, RAGGED_KV, 32, 8, 128, 16, 120, seed=1, device="cpu",
+                         scales="amax")
+    s = sub_workload(w, range(w.batch))
+    P, ps, H, D = s["num_pages"], 16, 8, 128
+    kc = np.zeros((P, ps, H, D // 2), np.uint8)
+    vc, ksf = np.zeros_like(kc), np.zeros((P, ps, H, D // 16), np.uint8)
+    vsf = np.zeros_like(ksf)
+    assert oracle.append(s["k"], s["v"], s["slots"], w.k_scale, w.v_scale, kc, vc, ksf, vsf, ps) == 0
+    rows = np.arange(P * ps * H)
+    kk = oracle.dequant_rows(kc.reshape(-1, 64), ksf.reshape(-1, 8), rows, D, w.k_scale)
+    vv = oracle.dequant_rows(vc.reshape(-1, 64), vsf.reshape(-1, 8), rows, D, w.v_scale)
+    d = M.dense_prefill(M._bf16_to_f64(s["q"]), kk, vv, s["qo"], s["kv_indptr"], s["page_table"], s["kv_lens"],
+                        ps, H, w.sm_scale)
+    ref, _ = oracle_outputs(oracle, w)
+    assert np.abs(d - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
+def _ratio_stats(O, w, mode):
     ref, _ = oracle_outputs(O, w)
-    emu, _ = M.mx_outputs(O, w)
+    emu, _ = M.mx_outputs(O, w, mode=mode)
     err = np.abs(emu - ref)
     return (err / (1 + np.abs(ref))).max(), np.sqrt((err ** 2).mean() / (ref ** 2).mean()), \
         (err / (1e-2 + 1e-2 * np.abs(ref))).max()
@@ -142,9 +192,10 @@ def _ratio_stats(O, w):
 
 @pytest.mark.parametrize("shape", ["uniform_256", "ragged_amax", "ragged_lognormal"])
 @pytest.mark.parametrize("seed", [1, 2])
-def test_mx_contract_on_the_emulation(oracle, shape, seed):
-    """The contract holds on the emulation with a margin of 1.5, and the
-    variant does leave the exact path's 1e-2 bound (so it needs its own)."""
+@pytest.mark.parametrize("mode", [4, 5])
+def test_mx_contract_on_the_emulation(oracle, shape, seed, mode):
+    """Each mode's contract holds on the emulation with a margin of 1.5, and
+    both leave the exact path's 1e-2 bound (so they need their own)."""
     if shape == "uniform_256":
         w = W.make_attention(shape, [256], [256], 32, 8, 128, 16, 20, seed=seed, device="cpu", scales="amax")
     elif shape == "ragged_amax":
@@ -153,9 +204,10 @@ def test_mx_contract_on_the_emulation(oracle, shape, seed):
     else:
         w = W.make_attention(shape, RAGGED_Q, RAGGED_KV, 32, 8, 128, 16, 120, seed=seed, device="cpu",
                              scales="lognormal", lognormal=(-3.0, 0.5))
-    elem, rms, tight = _ratio_stats(oracle, w)
-    assert elem * 1.5 <= M.MX_ELEM
-    assert rms * 1.5 <= M.MX_RMS
+    elem, rms, tight = _ratio_stats(oracle, w, mode)
+    elem_max, rms_max = M.MX_CONTRACT[mode]
+    assert elem * 1.5 <= elem_max
+    assert rms * 1.5 <= rms_max
     assert tight > 1.0
 
 
