@@ -202,8 +202,8 @@ def main():
         "config": {"workload": w.name, "batch": 1, "q_len": 2048, "kv_len": 2048,
                    "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128, "page_size": 16,
                    "kv_format": "nvfp4 (e2m1 + e4m3 per 16, fp32 global scale)",
-                   "staging": "f16 LDS tile, f16 MFMA (bf16 staging + bf16 MFMA: dequant_ablation "
-                              "lds_once_per_tile_bf16)",
+                   "staging": "f16 LDS tile, f16 MFMA (the bf16 form, bf16 staging + bf16 MFMA, is "
+                              "dequant_mode 3: configs.*.prefill_bf16)",
                    "step": "append 2048 K/V rows + causal paged prefill",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": kernel_name,
@@ -247,6 +247,8 @@ def main():
         c2.append(w2.k, w2.v, w2.slot_mapping)
         result["dequant_ablation"] = bench_dequant_ablation(K, w2, c2, (qo_d, kvp_d, pt_d, kvl_d),
                                                             torch.empty_like(w2.q), torch)
+        # the bf16 form on this batch (4-wave tiles, as the plan picks for it)
+        configs["prefill_2k"]["prefill_bf16"] = result["dequant_ablation"]["lds_once_per_tile_bf16"]
         del w2, c2
     if not args.no_achievable:
         ach = bench_achievable(W, dev, torch, np)
@@ -300,10 +302,14 @@ def bench_config_small(K, W, dev, torch):
                   w.num_kv_heads, w.head_dim, w.page_size)
     out = torch.empty_like(w.q)
     pre = graph_launch_ms(torch, lambda: K.paged_prefill_causal(w.q, *args, cache, out, w.sm_scale, plan=plan))
+    plan3 = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), w.num_q_heads,
+                   w.num_kv_heads, w.head_dim, w.page_size, dequant_mode=3)
+    pre3 = graph_launch_ms(torch, lambda: K.paged_prefill_causal(w.q, *args, cache, out, w.sm_scale, plan=plan3))
     app = graph_launch_ms(torch, lambda: cache.append(w.k, w.v, w.slot_mapping))
     flops = attention_flops(w.q_lens, w.kv_lens, w.num_q_heads, w.head_dim)
     nbytes = append_bytes(int(w.kv_lens.sum()), w.num_kv_heads, w.head_dim)
     return {"workload": w.name, "prefill": {"flops_per_launch": flops, **tflops_row(flops, pre)},
+            "prefill_bf16": {"dequant_mode": 3, **tflops_row(flops, pre3)},
             "append": {"bytes_per_launch": nbytes, **gbs_row(nbytes, app)},
             "note": "a few microseconds of work: bound by launch latency, not by the roofline"}
 
@@ -339,9 +345,14 @@ def bench_config_large(K, w, torch, chunk_append=False):
     plan = mk()
     pre = graph_launch_ms(torch, lambda: K.paged_prefill_causal(w.q, *args, cache, out, w.sm_scale, plan=plan),
                           per_graph=4, replays=3)
+    plan3 = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), w.num_q_heads,
+                   w.num_kv_heads, w.head_dim, w.page_size, dequant_mode=3)
+    pre3 = graph_launch_ms(torch, lambda: K.paged_prefill_causal(w.q, *args, cache, out, w.sm_scale, plan=plan3),
+                           per_graph=4, replays=3)
     row = {"workload": w.name, "prefill": {"flops_per_launch": flops, "schedule": plan.schedule,
                                            "block_q": plan.block_q, "split_len": plan.split_len,
                                            **tflops_row(flops, pre)},
+           "prefill_bf16": {"dequant_mode": 3, **tflops_row(flops, pre3)},
            "append": {"bytes_per_launch": nbytes, "rows": int(k.shape[0]), **gbs_row(nbytes, app)}}
     sched = {}
     for name, s in (("heaviest_first", K.SCHEDULE_HEAVIEST), ("stream_order", K.SCHEDULE_STREAM),

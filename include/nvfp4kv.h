@@ -144,7 +144,7 @@ typedef struct {
           hardware conversion;
        3  as 0 with a bf16 staging tile, bf16 queries and probabilities and
           bf16 matrix instructions (0 stages f16: exact as well, fewer
-          instructions);
+          instructions); every shape mode 0 has;
        4  native low-precision scores ([PR #4769] code analysis: the branch
           for matrix cores that take E2M1 operands): K requantized while
           staged from NVFP4 (E4M3 scale per 16) to MXFP4 (E8M0 scale per
@@ -157,8 +157,9 @@ typedef struct {
        5  as 4 with K requantized to MXFP8 (E4M3 elements): twice the
           staged K bytes, the same instruction rate, contract 0.3 and 0.05
           (typical per-row relative error about 3%).
-     1 to 5 exist for head_dim 128, GQA group 4, 4-wave tiles (block_q 32)
-     and page sizes dividing 64; other shapes return NVFP4KV_EUNSUPPORTED.
+     1, 2, 4 and 5 exist for head_dim 128, GQA group 4, 4-wave tiles
+     (block_q 32) and page sizes dividing 64; other shapes, and other mode
+     values, return NVFP4KV_EUNSUPPORTED before anything is launched.
      0 to 3 give results within the same tolerance of the oracle (0, 1 and
      2 bit-identical). */
   int32_t dequant_mode;

@@ -343,7 +343,7 @@ def plan(qo_indptr, kv_lens, num_q_heads, num_kv_heads, head_dim, page_size, kv_
     of 32 query rows per workgroup (0 automatic, 4 or 8); dequant_mode: the
     dequant-placement ablation (0: tiles decoded once into f16 LDS, the
     default; 1: K decoded in registers inside the matrix loop; 2: byte-table
-    decode; 3: bf16 staging and bf16 matrix instructions; 4 and 5: native
+    decode; 3: bf16 staging and bf16 matrix instructions, for every shape; 4 and 5: native
     MX scores -- MXFP4 (4) or MXFP8 (5) keys, MXFP8 queries, the scaled
     matrix instruction, under looser accuracy contracts); schedule: issue
     order of the Q tiles (0: the plan's choice; SCHEDULE_HEAVIEST,

@@ -659,8 +659,8 @@ __device__ __forceinline__ Item decode_item(const PrefillArgs& a, uint32_t tile)
 // after an exact power-of-two rescale of the row: bf16 values have 8
 // significant bits, and the row's largest magnitude goes to [2^14, 2^15), so
 // every value within 2^-28 of it stays a normal f16.  The row's scale comes
-// back in its score scale, returned (scores -> log2 domain).  DQ 3: bf16
-// fragments as they are.
+// back in its score scale, returned (scores -> log2 domain).  DQ 3: the same
+// rescale, the fragments in bf16 (exact; raw scores keep the same bound).
 template <int D, int DQ>
 __device__ __forceinline__ float load_q(const uint16_t* qrow, int hh, float score_scale, f16x8 (&qf)[D / 16]) {
   constexpr int NDC = D / 16;
@@ -673,14 +673,18 @@ __device__ __forceinline__ float load_q(const uint16_t* qrow, int hh, float scor
     for (int e = 0; e < 4; ++e) am = max(am, max(qw[c][e] & 0x7FFFu, (qw[c][e] >> 16) & 0x7FFFu));
   }
   am = max(am, (uint32_t)__shfl_xor((int)am, 32));  // the row's other half
-  const int sh = DQ == 3 ? 0 : am >= 0x80u ? min(max((int)(am >> 7) - 127 - 14, -100), 113) : 0;
+  const int sh = am >= 0x80u ? min(max((int)(am >> 7) - 127 - 14, -100), 113) : 0;
   const float down = u2f((uint32_t)(127 - sh) << 23);  // 2^-sh
 #pragma unroll
   for (int c = 0; c < NDC; ++c)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if constexpr (DQ != 3) {  // (bf16 matrix instructions take the bf16 bits as they are)
-        const f16x2 h = {(_Float16)(u2f(qw[c][e] << 16) * down), (_Float16)(u2f(qw[c][e] & 0xFFFF0000u) * down)};
+      const float lo = u2f(qw[c][e] << 16) * down, hi = u2f(qw[c][e] & 0xFFFF0000u) * down;
+      if constexpr (DQ == 3) {  // bf16 matrix instructions: the same rescale, exact in bf16 (RNE below its normals)
+        const bf16x2 h = {(__bf16)lo, (__bf16)hi};
+        qw[c][e] = __builtin_bit_cast(uint32_t, h);
+      } else {
+        const f16x2 h = {(_Float16)lo, (_Float16)hi};
         qw[c][e] = __builtin_bit_cast(uint32_t, h);
       }
     }
@@ -1317,12 +1321,12 @@ __global__ __launch_bounds__(1024) void worklist_kernel(const int32_t* __restric
   }
 }
 
-template <int D, int G, int W>
+template <int D, int G, int W, int DQ>
 void launch_prefill(const PrefillArgs& a, hipStream_t s) {
   if (kBlockN % a.ps_div.d == 0)
-    hipLaunchKernelGGL((prefill_kernel<D, G, W, true, 0>), dim3(a.num_items), dim3(64 * W), 0, s, a);
+    hipLaunchKernelGGL((prefill_kernel<D, G, W, true, DQ>), dim3(a.num_items), dim3(64 * W), 0, s, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, G, W, false, 0>), dim3(a.num_items), dim3(64 * W), 0, s, a);
+    hipLaunchKernelGGL((prefill_kernel<D, G, W, false, DQ>), dim3(a.num_items), dim3(64 * W), 0, s, a);
 }
 
 }  // namespace
@@ -1382,6 +1386,19 @@ extern "C" int paged_prefill_causal(const void* q, const int32_t* qo_indptr,
   a.nxcd = p.num_xcd > 0 ? p.num_xcd : 1;
   a.num_tiles = (uint32_t)p.num_tiles;
   a.num_items = (uint32_t)p.num_items;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int D = p.head_dim;
+  const int W = p.block_q * G / 32;  // waves per tile chosen by the plan
+  // every kernel this call could launch exists, or nothing is launched
+  const bool g_ok = G == 1 || G == 2 || G == 4 || G == 8;
+  const bool shape_ok = g_ok && ((D == 128 && (W == 4 || W == 8)) || (D == 64 && W == 4));
+  // bf16 staging (mode 3) for every kernel shape; the other modes of the
+  // dequant-placement ablation and the MX score modes for head_dim 128, GQA
+  // group 4, 4-wave tiles and page sizes dividing the KV tile
+  const bool mode_ok = p.dequant_mode == 0 || p.dequant_mode == 3 ||
+                       (p.dequant_mode >= 1 && p.dequant_mode <= 5 && D == 128 && G == 4 && W == 4 &&
+                        kBlockN % c.page_size == 0);
+  if (!shape_ok || !mode_ok) return NVFP4KV_EUNSUPPORTED;
   const WorkspaceLayout wl = workspace_layout(p);
   // the heavy/light pairing assumes two co-resident workgroups per CU
   a.snake = p.block_q * (p.num_q_heads / p.num_kv_heads) == 128 &&
@@ -1396,29 +1413,22 @@ extern "C" int paged_prefill_causal(const void* q, const int32_t* qo_indptr,
                        p.num_kv_heads, p.block_q, p.q_tiles_per_head, p.split_len, p.schedule,
                        (int4*)workspace, a.counters, 2 * p.num_split_tiles);
   }
-  const int G = p.num_q_heads / p.num_kv_heads;
-  const int D = p.head_dim;
-  const int W = p.block_q * G / 32;  // waves per tile chosen by the plan
-  if (p.dequant_mode != 0) {
-    // dequant-placement ablation: head_dim 128, GQA group 4, 4-wave tiles,
-    // page sizes dividing the KV tile
-    if (D != 128 || G != 4 || W != 4 || kBlockN % c.page_size != 0 || p.dequant_mode < 1 ||
-        p.dequant_mode > 5)
-      return NVFP4KV_EUNSUPPORTED;
+  if (p.dequant_mode != 0 && p.dequant_mode != 3) {
     if (p.dequant_mode == 1)
       hipLaunchKernelGGL((prefill_kernel<128, 4, 4, true, 1>), dim3(a.num_items), dim3(256), 0, s, a);
     else if (p.dequant_mode == 2)
       hipLaunchKernelGGL((prefill_kernel<128, 4, 4, true, 2>), dim3(a.num_items), dim3(256), 0, s, a);
-    else if (p.dequant_mode == 3)
-      hipLaunchKernelGGL((prefill_kernel<128, 4, 4, true, 3>), dim3(a.num_items), dim3(256), 0, s, a);
     else if (p.dequant_mode == 4)
       hipLaunchKernelGGL((prefill_kernel<128, 4, 4, true, 4>), dim3(a.num_items), dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL((prefill_kernel<128, 4, 4, true, 5>), dim3(a.num_items), dim3(256), 0, s, a);
     return hipGetLastError() == hipSuccess ? NVFP4KV_OK : NVFP4KV_EHIP;
   }
-#define NVFP4KV_CASE(DD, GG, WW) \
-  if (D == DD && G == GG && W == WW) launch_prefill<DD, GG, WW>(a, s); else
+#define NVFP4KV_CASE(DD, GG, WW)                                                    \
+  if (D == DD && G == GG && W == WW) {                                              \
+    if (p.dequant_mode == 3) launch_prefill<DD, GG, WW, 3>(a, s);                  \
+    else launch_prefill<DD, GG, WW, 0>(a, s);                                       \
+  } else
   NVFP4KV_CASE(128, 1, 4) NVFP4KV_CASE(128, 2, 4) NVFP4KV_CASE(128, 4, 4) NVFP4KV_CASE(128, 8, 4)
   NVFP4KV_CASE(128, 1, 8) NVFP4KV_CASE(128, 2, 8) NVFP4KV_CASE(128, 4, 8) NVFP4KV_CASE(128, 8, 8)
   NVFP4KV_CASE(64, 1, 4) NVFP4KV_CASE(64, 2, 4) NVFP4KV_CASE(64, 4, 4) NVFP4KV_CASE(64, 8, 4)

@@ -304,11 +304,20 @@ def test_prefill_bf16_staging_2k(K, oracle):
     assert_close(out.index_select(0, torch.from_numpy(rows).cuda()), ref, w.name)
 
 
-def test_prefill_dequant_ablation_unsupported_shape(K):
-    """The ablation kernels exist for head_dim 128, GQA group 4, 4-wave tiles
-    only: other shapes are refused before any launch."""
+@pytest.mark.parametrize("mode", [1, 2, 4, 5, 6])
+def test_prefill_dequant_ablation_unsupported_shape(K, mode):
+    """The in-loop and byte-table ablation kernels and the MX score kernels
+    exist for head_dim 128, GQA group 4, 4-wave tiles only (the bf16 form,
+    mode 3, for every shape), and modes above 5 not at all: other requests
+    are refused before any launch."""
     w = W.make_attention("dequant_mode_d64", [64], [64], 8, 2, 64, 16, 8, seed=20, device="cuda")
     plan = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), 8, 2, 64, 16,
-                  dequant_mode=1)
+                  dequant_mode=mode)
     with pytest.raises(K.NVFP4KVError, match="unsupported"):
         run_gpu(K, w, plan=plan)
+    if mode == 6:  # not a mode even on the supported shape
+        w2 = W.make_attention("dequant_mode_6", [64], [64], 32, 8, 128, 16, 8, seed=20, device="cuda")
+        plan2 = K.plan(torch.from_numpy(w2.qo_indptr), torch.from_numpy(w2.kv_lens), 32, 8, 128, 16,
+                       tile_waves=4, dequant_mode=mode)
+        with pytest.raises(K.NVFP4KVError, match="unsupported"):
+            run_gpu(K, w2, plan=plan2)
