@@ -5,7 +5,8 @@ decode step (several chunks, so the merge kernel runs too).  Every replay
 follows fresh inputs written by ordinary eager copies, and its outputs must
 equal, bit for bit, the same calls made eagerly on the same inputs; the eager
 results themselves are held to the oracle by the other GPU tests, and once
-here on the first inputs."""
+here on the first inputs.  The prefill's bf16 form and its two MX score
+variants get the same replay check on their own."""
 import numpy as np
 import pytest
 import torch
@@ -92,4 +93,56 @@ def test_graph_replays_match_eager(K, oracle):
         if r == 0:
             ref, rows = oracle_outputs(oracle, w)
             assert_close(got_p.index_select(0, torch.from_numpy(rows).cuda()), ref, w.name)
+        print(f"replay {r}: bit-identical to eager", flush=True)
+
+
+@pytest.mark.parametrize("mode", [3, 4, 5])
+def test_graph_prefill_other_modes(K, mode):
+    """The bf16 form (mode 3) and the MX score modes (4, 5) under graph
+    capture, with split Q tiles: three replays, each after fresh queries
+    written eagerly, bit-identical to the same call made eagerly."""
+    banner(f"graph capture of the prefill in dequant mode {mode}, 3 replays")
+    w = W.make_attention(f"graph_mode_{mode}", [96, 300, 1, 517], [200, 300, 700, 1100], 16, 4, 128, 16, 160,
+                         seed=32, device="cuda", scales="amax")
+    dev = "cuda"
+    cache = gpu_cache(K, w)
+    cache.append(w.k, w.v, w.slot_mapping)
+    qo, kvp, pt, kvl = (torch.from_numpy(x).to(dev) for x in (w.qo_indptr, w.kv_indptr, w.page_table, w.kv_lens))
+    plan = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), w.num_q_heads, w.num_kv_heads,
+                  w.head_dim, w.page_size, kv_indptr=torch.from_numpy(w.kv_indptr), split_len=3, tile_waves=4,
+                  dequant_mode=mode)
+    assert plan.num_split_tiles > 0
+    q = w.q.clone()
+    out = torch.empty_like(q)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def step(o):
+        K.paged_prefill_causal(q, qo, kvp, pt, kvl, cache, o, w.sm_scale, plan=plan, dev_error=err)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(out)
+    torch.cuda.synchronize()
+    eager = torch.empty_like(out)
+    prev = None
+    for r in range(3):
+        if r > 0:
+            q.copy_(_fresh(q.shape, 50 + r, 0))
+        out.fill_(0)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        step(eager)
+        torch.cuda.synchronize()
+        assert K.read_device_error(word=err) == 0
+        assert torch.equal(got.view(torch.int16), eager.view(torch.int16)), f"replay {r}"
+        if prev is not None:
+            assert not torch.equal(got, prev), "replay produced the previous outputs"
+        prev = got
         print(f"replay {r}: bit-identical to eager", flush=True)
