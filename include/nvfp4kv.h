@@ -293,16 +293,21 @@ typedef struct {
   int64_t total_kv;
   int32_t chunk_len;        /* keys per KV chunk (a multiple of 64) */
   int32_t max_chunks;       /* chunks of the longest request */
-  int64_t num_items;        /* waves launched: batch x num_kv_heads x max_chunks */
+  int64_t num_items;        /* waves launched: batch x (num_kv_heads / heads_per_wave) x max_chunks */
   int64_t workspace_bytes;  /* chunk partials (0 when no request has two chunks) */
+  int32_t heads_per_wave;   /* adjacent KV heads per wave: 2 (head_dim 128) or 4
+                               (head_dim 64) when num_kv_heads allows and their
+                               query heads number at most 16, else fewer */
 } nvfp4kv_decode_plan;
 
 /*
  * nvfp4_decode_plan -- host-only plan of a decode step: every request has one
  * new query token (already appended to the cache) that attends to all of its
  * kv_len keys.  The KV range of a request is cut into chunks of chunk_len
- * keys, one wave per (request, chunk, KV head), so that short batches still
- * fill the GPU; the chunks' partial results are merged in chunk order.
+ * keys, one wave per (request, chunk, group of heads_per_wave adjacent KV
+ * heads: their slices of a token's code row fill one 128-byte line, so each
+ * line has one reader), so that short batches still fill the GPU; the
+ * chunks' partial results are merged in chunk order.
  *   kv_lens_host  int32 [batch], each >= 1.
  *   chunk_len     keys per chunk: 0 = automatic (at least 256, enough chunks
  *                 for about 8 waves per CU), else a positive multiple of 64.

@@ -72,7 +72,8 @@ class DecodePlanStruct(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("batch", "num_q_heads", "num_kv_heads", "head_dim", "page_size", "max_kv_len")] + \
                [("total_kv", ctypes.c_int64), ("chunk_len", ctypes.c_int32), ("max_chunks", ctypes.c_int32),
-                ("num_items", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+                ("num_items", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
+                ("heads_per_wave", ctypes.c_int32)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -200,19 +200,22 @@ extern "C" int nvfp4_decode_plan(const int32_t* kv_lens_host, int32_t batch, int
   if (bad) return NVFP4KV_ERANGE;
   p.max_kv_len = max_kv;
   p.total_kv = tot_kv;
+  // One wave per (request, chunk, group of heads_per_wave KV heads).
   // Chunks: at least kDecodeMinChunk keys (the merge costs one partial per
   // chunk), and enough of them for about kDecodeWavesPerCu waves per CU.
+  p.heads_per_wave = decode_heads_per_wave(head_dim, G, num_kv_heads);
+  const int64_t groups = num_kv_heads / p.heads_per_wave;
   int64_t len = chunk_len;
   if (len == 0) {
     const int64_t target = (int64_t)kDecodeWavesPerCu * device_props().cu_count;
-    len = (tot_kv * num_kv_heads + target - 1) / std::max<int64_t>(target, 1);
+    len = (tot_kv * groups + target - 1) / std::max<int64_t>(target, 1);
     len = std::max<int64_t>((len + kBlockN - 1) / kBlockN * kBlockN, kDecodeMinChunk);
   }
   len = std::max<int64_t>(len, ((int64_t)max_kv + kDecodeMaxChunks - 1) / kDecodeMaxChunks);
   len = (len + kBlockN - 1) / kBlockN * kBlockN;
   p.chunk_len = (int32_t)std::min<int64_t>(len, 1 << 30);
   p.max_chunks = batch > 0 ? (int32_t)((max_kv + p.chunk_len - 1) / p.chunk_len) : 0;
-  p.num_items = (int64_t)batch * num_kv_heads * p.max_chunks;
+  p.num_items = (int64_t)batch * groups * p.max_chunks;
   p.workspace_bytes = decode_workspace_bytes(p);
   *plan = p;
   return NVFP4KV_OK;
@@ -244,4 +247,4 @@ extern "C" const char* nvfp4kv_status_string(int status) {
   }
 }
 
-extern "C" int nvfp4kv_abi_version(void) { return 102; }
+extern "C" int nvfp4kv_abi_version(void) { return 103; }

@@ -72,6 +72,14 @@ constexpr int kDecodeMinChunk = 256;
 constexpr int kDecodeMaxChunks = 4096;
 constexpr int kDecodeWavesPerCu = 8;
 constexpr int64_t decode_partial_floats(int head_dim) { return head_dim + 4; }
+// KV heads per decode wave: as many adjacent heads as fill one 128-byte line
+// of a token's code row (head_dim / 2 bytes each), while their query heads
+// fit the 16 columns of the score MFMA and the head count divides evenly.
+constexpr int decode_heads_per_wave(int head_dim, int group, int num_kv_heads) {
+  int hp = 256 / head_dim;
+  while (hp > 1 && (hp * group > 16 || num_kv_heads % hp != 0)) hp /= 2;
+  return hp;
+}
 inline int64_t decode_workspace_bytes(const nvfp4kv_decode_plan& p) {
   return p.max_chunks > 1 ? (int64_t)p.batch * p.num_q_heads * p.max_chunks *
                                 decode_partial_floats(p.head_dim) * 4

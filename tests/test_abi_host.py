@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol(K):
     L = ctypes.CDLL(K.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert K.lib().nvfp4kv_abi_version() == 102
+    assert K.lib().nvfp4kv_abi_version() == 103
     assert K.lib().nvfp4kv_status_string(-3).startswith(b"inconsistent")
 
 
@@ -181,11 +181,13 @@ def test_decode_plan_chunks_and_workspace(K):
     kv = torch.tensor([1, 300, 4096, 65], dtype=torch.int32)
     p = K.decode_plan(kv, 32, 8, 128, 16)
     assert p.chunk_len % 64 == 0 and p.chunk_len >= 256
-    assert p.max_chunks == -(-4096 // p.chunk_len) and p.num_items == 4 * 8 * p.max_chunks
+    # two KV heads per wave (head_dim 128: 2 x 64 code bytes fill a 128-byte line)
+    assert p.heads_per_wave == 2
+    assert p.max_chunks == -(-4096 // p.chunk_len) and p.num_items == 4 * 4 * p.max_chunks
     assert p.max_kv_len == 4096 and p.total_kv == int(kv.sum())
     assert p.workspace_bytes == (4 * 32 * p.max_chunks * (128 + 4) * 4 if p.max_chunks > 1 else 0)
     q = K.decode_plan(kv, 32, 8, 128, 16, chunk_len=128)
-    assert q.chunk_len == 128 and q.max_chunks == 32 and q.num_items == 4 * 8 * 32
+    assert q.chunk_len == 128 and q.max_chunks == 32 and q.num_items == 4 * 4 * 32
     q = K.decode_plan(torch.tensor([100, 20], dtype=torch.int32), 8, 2, 64, 16, chunk_len=128)
     assert q.max_chunks == 1 and q.workspace_bytes == 0
     with pytest.raises(ValueError):
@@ -196,6 +198,20 @@ def test_decode_plan_chunks_and_workspace(K):
         K.decode_plan(kv, 24, 8, 128, 16)                  # GQA group 3
     p = K.decode_plan(torch.tensor([], dtype=torch.int32), 32, 8, 128, 16)
     assert p.num_items == 0 and p.workspace_bytes == 0
+
+
+@pytest.mark.parametrize("hq,hk,d,hp", [
+    (32, 8, 128, 2), (64, 8, 128, 2), (8, 8, 128, 2), (3, 3, 128, 1), (4, 1, 128, 1), (6, 3, 128, 1),
+    (16, 8, 64, 4), (16, 4, 64, 4), (8, 8, 64, 4), (64, 8, 64, 2), (16, 2, 64, 2), (12, 6, 64, 2),
+    (8, 1, 64, 1), (5, 5, 64, 1)])
+def test_decode_plan_heads_per_wave(K, hq, hk, d, hp):
+    """Adjacent KV heads per decode wave: as many as fill a 128-byte line of
+    the code row (256 / head_dim), halved until the wave's query heads fit 16
+    columns and the count divides the KV heads; the wave count follows."""
+    kv = torch.tensor([700, 64, 1], dtype=torch.int32)
+    p = K.decode_plan(kv, hq, hk, d, 16, chunk_len=256)
+    assert p.heads_per_wave == hp
+    assert p.num_items == 3 * (hk // hp) * 3
 
 
 def test_plan_empty_requests(K):
