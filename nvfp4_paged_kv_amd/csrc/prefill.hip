@@ -153,9 +153,15 @@ __device__ __forceinline__ float coherent_load1(__amdgpu_buffer_rsrc_t r, int of
 }
 
 // max(x, x of lane l ^ 32) in every lane: one v_permlane32_swap exchanges
-// the wave's halves in registers (no LDS round trip).
+// the wave's halves in registers (no LDS round trip).  The swap is given
+// two registers that hold x: its results are x and the other half's x.  The
+// second copy goes through an empty asm so that the optimizer cannot see the
+// two operands are the same value (it then takes the swap's two results for
+// equal and drops the max).
 __device__ __forceinline__ float half_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+  uint32_t y = f2u(x);
+  asm volatile("" : "+v"(y));
+  const auto r = __builtin_amdgcn_permlane32_swap(f2u(x), y, false, false);
   return __builtin_fmaxf(u2f(r[0]), u2f(r[1]));
 }
 

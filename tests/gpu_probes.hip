@@ -171,6 +171,20 @@ __global__ void fp4_from_f16_kernel(uint32_t* out) {
   out[t] = o;
 }
 
+// The cross-row lane swaps the decode's softmax uses for its column maxima:
+// one wave, x = in[lane] as both operands; out holds, per lane, the two
+// results of v_permlane16_swap then those of v_permlane32_swap.
+__global__ void permlane_swap_kernel(const uint32_t* in, uint32_t* out) {
+  const int l = threadIdx.x;
+  const uint32_t x = in[l];
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  out[l] = a[0];
+  out[64 + l] = a[1];
+  out[128 + l] = b[0];
+  out[192 + l] = b[1];
+}
+
 extern "C" {
 // All pointers are device pointers; every call synchronizes the device.
 int probe_e2m1_scan(uint32_t sign, int mode, uint32_t* count, uint32_t* buf, uint32_t cap) {
@@ -205,6 +219,10 @@ int probe_fp4_from_f16(uint32_t* out) {  // out: 8192 words
 }
 int probe_mfma_scale(const int* a, const int* b, const int* sa, const int* sb, float* d) {
   mfma_scale_kernel<<<1, 64>>>(a, b, sa, sb, d);
+  return hipDeviceSynchronize() == hipSuccess ? 0 : -1;
+}
+int probe_permlane_swap(const uint32_t* in, uint32_t* out) {  // in: 64 words, out: 256
+  permlane_swap_kernel<<<1, 64>>>(in, out);
   return hipDeviceSynchronize() == hipSuccess ? 0 : -1;
 }
 int probe_mfma16(const float* A, const float* B, float* D) {

@@ -2,8 +2,9 @@
 tests/libnvfp4kv_probes.so): the hardware FP4 conversion used by the append
 against the oracle's E2M1 encoder over every fp32 pattern, the FP4 -> fp32
 decode used by the attention's staging, the E4M3 pair decode of its block
-scales, the MFMA lane layouts, and what the MX score variant relies on: the
-scaled FP4 x FP8 matrix instruction and the two encoders that feed it."""
+scales, the MFMA lane layouts, the cross-row lane swaps, and what the MX
+score variant relies on: the scaled FP4 x FP8 matrix instruction and the two
+encoders that feed it."""
 import ctypes
 import os
 
@@ -24,7 +25,8 @@ def probes():
         pytest.fail("tests/libnvfp4kv_probes.so missing: run __graft_entry__.build()")
     L = ctypes.CDLL(path)
     for f in ("probe_e2m1_scan", "probe_cvt_pairs", "probe_fp4_to_bf16", "probe_mfma32", "probe_mfma16",
-              "probe_fp8_pairs", "probe_mfma_scale", "probe_fp8_from_bf16", "probe_fp4_from_f16"):
+              "probe_fp8_pairs", "probe_mfma_scale", "probe_fp8_from_bf16", "probe_fp4_from_f16",
+              "probe_permlane_swap"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -123,6 +125,29 @@ def test_mfma_32x32x16_layout(probes):
     Ad, Bd, Dd = A.cuda(), B.cuda(), D.cuda()
     assert probes.probe_mfma32(P(Ad), P(Bd), P(Dd)) == 0
     torch.testing.assert_close(Dd.cpu(), A.double().mm(B.double()).float(), rtol=1e-5, atol=1e-5)
+
+
+def test_permlane_swaps_exchange_rows(probes):
+    """v_permlane16_swap with one register as both operands leaves lanes of
+    even 16-lane rows their own value in the first result and the value of
+    lane + 16 in the second (odd rows: lane - 16, then their own), so the
+    pair is {x[l], x[l ^ 16]} in every lane; v_permlane32_swap likewise
+    with the wave's halves, {x[l], x[l ^ 32]}."""
+    x = torch.arange(1000, 1064, dtype=torch.int32)
+    xd, out = x.cuda(), torch.zeros(256, dtype=torch.int32, device="cuda")
+    assert probes.probe_permlane_swap(P(xd), P(out)) == 0
+    o = out.cpu().view(4, 64).numpy()
+    xs = x.numpy()
+    lane = np.arange(64)
+    even16 = (lane // 16) % 2 == 0
+    np.testing.assert_array_equal(o[0], np.where(even16, xs[lane], xs[lane - 16]))
+    np.testing.assert_array_equal(o[1], np.where(even16, xs[(lane + 16) % 64], xs[lane]))
+    lo = lane < 32
+    np.testing.assert_array_equal(o[2], np.where(lo, xs[lane], xs[lane - 32]))
+    np.testing.assert_array_equal(o[3], np.where(lo, xs[(lane + 32) % 64], xs[lane]))
+    for a, b, k in ((o[0], o[1], 16), (o[2], o[3], 32)):
+        np.testing.assert_array_equal(np.minimum(a, b), np.minimum(xs, xs[lane ^ k]))
+        np.testing.assert_array_equal(np.maximum(a, b), np.maximum(xs, xs[lane ^ k]))
 
 
 def test_mfma_16x16x32_layout(probes):
