@@ -60,6 +60,27 @@ def test_decode_ragged_all_kernels(K, oracle, hq, hk, d):
     print(f"max err {e:.3g}; chunk_len {plan.chunk_len}, chunks {plan.max_chunks}")
 
 
+# every (head_dim, GQA group, heads per wave) kernel: odd KV head counts take
+# one head per wave, head_dim 128 two, head_dim 64 four when the KV heads and
+# the 16 score columns allow
+EVERY_HP = [(1, 1, 128, 1), (6, 3, 128, 1), (12, 3, 128, 1), (24, 3, 128, 1),
+            (2, 2, 128, 2), (4, 2, 128, 2), (8, 2, 128, 2), (16, 2, 128, 2),
+            (3, 3, 64, 1), (6, 3, 64, 1), (12, 3, 64, 1), (24, 3, 64, 1),
+            (2, 2, 64, 2), (4, 2, 64, 2), (8, 2, 64, 2), (16, 2, 64, 2),
+            (4, 4, 64, 4), (8, 4, 64, 4), (16, 4, 64, 4)]
+
+
+@pytest.mark.parametrize("hq,hk,d,hp", EVERY_HP)
+def test_decode_every_heads_per_wave_kernel(K, oracle, hq, hk, d, hp):
+    """Each kernel instance against the oracle, with several chunks per
+    request (forced 128-key chunks) and lengths ending inside a tile."""
+    banner(f"decode hq={hq} hk={hk} d={d}: {hp} KV heads per wave")
+    kv = [1, 31, 33, 129, 300, 517]
+    e, plan = _check(K, oracle, _ragged(hq, hk, d, seed=29, kv=kv), chunk_len=128)
+    assert plan.heads_per_wave == hp and plan.max_chunks == 5
+    print(f"max err {e:.3g}")
+
+
 @pytest.mark.parametrize("chunk_len", [64, 128, 192, 1024])
 def test_decode_forced_chunks(K, oracle, chunk_len):
     """Chunks merged in order: one tile per chunk, uneven last chunks,
