@@ -251,12 +251,15 @@ def main():
         configs["prefill_2k"]["prefill_bf16"] = result["dequant_ablation"]["lds_once_per_tile_bf16"]
         del w2, c2
     if not args.no_achievable:
-        ach = bench_achievable(W, dev, torch, np)
+        ach = bench_achievable(K, W, dev, torch, np)
         ach["prefill_frac_of_mfma_loop"] = round(pre_tflops / ach["mfma_bf16_TFLOPs"], 4)
         if "append_stress" in result:
             got = result["append_stress"]["achieved_GBps"]
             ach["append_stress_frac_of_copy"] = round(got / ach["copy_GBps"], 4)
             ach["append_stress_frac_of_traffic_probe"] = round(got / ach["append_traffic_GBps"], 4)
+        if "decode" in result and "decode_traffic_1_ahead_GBps" in ach:
+            got = result["decode"]["achieved_GBps"]
+            ach["decode_frac_of_traffic_probe"] = round(got / ach["decode_traffic_1_ahead_GBps"], 4)
         result["achievable"] = ach
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, flops, W, dev, torch, np)
@@ -500,16 +503,19 @@ def bench_decode(K, W, dev, torch, np, iters=12, per_graph=20, replays=3):
             "cache": "cold (flushed)", "traffic": _traffic("decode")}
 
 
-def bench_achievable(W, dev, torch, np):
+def bench_achievable(K, W, dev, torch, np):
     """Measured achievable rates on this device.  Cold, like the append and
     decode figures (the 256 MB Infinity Cache flushed by an untimed 512 MiB
     read before every launch; median of 12 launches, HIP events on the launch
     stream): a 16-byte-per-lane copy of 128 MiB (read + write bytes / time),
-    and the 65,536-token append's own data movement without its arithmetic
+    the 65,536-token append's own data movement without its arithmetic
     (peak.hip append_traffic: the same bf16 loads and the same code and
     scale stores through the same scattered slots; the append's algorithmic
-    bytes / time).  Warm: the MFMA-only loop of peak.hip (dense
-    v_mfma_f32_32x32x16_bf16, two waves per SIMD; median of 10)."""
+    bytes / time), and the 32 x 8192 decode's reads without its arithmetic
+    (peak.hip decode_traffic: the same waves, page lookups and per-lane
+    loads, with one tile in flight as the decode has, and with two; the
+    decode's algorithmic bytes / time).  Warm: the MFMA-only loop of peak.hip
+    (dense v_mfma_f32_32x32x16_bf16, two waves per SIMD; median of 10)."""
     import ctypes
     from nvfp4_paged_kv_amd.build import PEAK_LIB
     if not os.path.exists(PEAK_LIB):
@@ -557,7 +563,31 @@ def bench_achievable(W, dev, torch, np):
         stream), "append traffic"), n=12, cold=True)
     out["append_traffic_GBps"] = round(append_bytes(a.k.shape[0], a.num_kv_heads, a.head_dim)
                                        / traffic_s / 1e9, 1)
-    del a, cache, flush
+    del a, cache
+
+    w = W.decode_batch(dev)
+    dcache = K.PagedCache.empty(w.num_pages, w.page_size, w.num_kv_heads, w.head_dim, dev,
+                                w.k_scale, w.v_scale)
+    dcache.append(w.k, w.v, w.slot_mapping)
+    dplan = K.decode_plan(torch.from_numpy(w.kv_lens), w.num_q_heads, w.num_kv_heads, w.head_dim,
+                          w.page_size)
+    if w.head_dim == 128 and dplan.heads_per_wave == 2:
+        kvp, pt, kvl = (torch.from_numpy(x).to(dev) for x in (w.kv_indptr, w.page_table, w.kv_lens))
+        words = torch.empty(dplan.num_items * 64, dtype=torch.int32, device=dev)
+        L.nvfp4kv_decode_traffic_probe.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                                   ctypes.c_int64, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp,
+                                                   vp, ctypes.c_int, vp]
+        dbytes = (int(w.kv_lens.sum()) * w.num_kv_heads * (w.head_dim // 2 + w.head_dim // 16) * 2
+                  + 2 * w.q.numel() * 2)
+        for ahead in (1, 2):
+            t = timed(lambda: check(L.nvfp4kv_decode_traffic_probe(
+                vp(kvp.data_ptr()), vp(pt.data_ptr()), vp(kvl.data_ptr()), dplan.num_items, w.num_kv_heads,
+                w.page_size, w.num_pages, dplan.chunk_len, dplan.max_chunks,
+                *(vp(c.data_ptr()) for c in (dcache.k_cache, dcache.v_cache, dcache.k_sf, dcache.v_sf)),
+                vp(words.data_ptr()), ahead, stream), "decode traffic"), n=12, cold=True)
+            out[f"decode_traffic_{ahead}_ahead_GBps"] = round(dbytes / t / 1e9, 1)
+        del kvp, pt, kvl, words
+    del w, dcache, flush
 
     L.nvfp4kv_mfma_peak_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     L.nvfp4kv_mfma_peak_probe_flops.restype = ctypes.c_double
