@@ -214,6 +214,27 @@ def test_decode_plan_heads_per_wave(K, hq, hk, d, hp):
     assert p.num_items == 3 * (hk // hp) * 3
 
 
+@pytest.mark.parametrize("field,value", [("heads_per_wave", 1), ("heads_per_wave", 4), ("num_items", -1),
+                                         ("num_items", +1)])
+def test_decode_rejects_a_plan_whose_waves_do_not_match_its_shape(K, field, value):
+    """paged_decode maps every wave below num_items to a (request, chunk, head
+    group); a plan whose heads_per_wave or num_items differs from what its
+    shape gives is refused with EINVAL before anything is launched (the
+    pointers here are placeholders that are never dereferenced)."""
+    kv = torch.tensor([700, 64, 1], dtype=torch.int32)
+    p = K.decode_plan(kv, 32, 8, 128, 16, chunk_len=256)
+    st = K.DecodePlanStruct.from_buffer_copy(p.struct)
+    if field == "heads_per_wave":
+        st.heads_per_wave = value
+    else:
+        st.num_items = st.num_items + value
+    fake = ctypes.c_void_p(1 << 20)  # 16-byte aligned, never touched
+    cache = K.Cache(1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 64, 16, 8, 128)
+    rc = K.lib().paged_decode(fake, fake, fake, fake, ctypes.byref(cache), fake, ctypes.c_float(0.088),
+                              ctypes.byref(st), fake, ctypes.c_int64(1 << 30), fake, None)
+    assert rc == K.EINVAL
+
+
 def test_plan_empty_requests(K):
     p = _plan(K, [0, 0, 5], [7, 5])
     assert p.max_q_len == 5 and p.total_q == 5 and p.num_tiles == 8 and p.uniform_q == 0
