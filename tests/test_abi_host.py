@@ -214,6 +214,15 @@ def test_decode_plan_heads_per_wave(K, hq, hk, d, hp):
     assert p.num_items == 3 * (hk // hp) * 3
 
 
+def test_decode_plan_fills_one_round_of_waves(K):
+    """32 requests x 8192 keys, 32/8 heads, head_dim 128 on 256 CUs: two KV
+    heads per wave, 512-key chunks, 16 chunks per request, 2,048 waves (eight
+    per CU, one round of the 8-wave workgroups)."""
+    p = K.decode_plan(torch.full((32,), 8192, dtype=torch.int32), 32, 8, 128, 16)
+    assert (p.heads_per_wave, p.chunk_len, p.max_chunks, p.num_items) == (2, 512, 16, 2048)
+    assert p.workspace_bytes == 32 * 32 * 16 * (128 + 4) * 4
+
+
 @pytest.mark.parametrize("field,value", [("heads_per_wave", 1), ("heads_per_wave", 4), ("num_items", -1),
                                          ("num_items", +1)])
 def test_decode_rejects_a_plan_whose_waves_do_not_match_its_shape(K, field, value):
