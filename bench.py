@@ -17,7 +17,8 @@ divided by the step time).  Also reported:
   * configs: every workload (the 2x128 small batch, the 2048x2048 prefill,
     the 1024x1024 uniform batch, the ragged chunked-prefill batch, the
     65,536-token append) with its prefill TFLOP/s and append GB/s and their
-    fractions of the MI355X roofline;
+    fractions of the MI355X roofline, and the prefill kernel on equal-cost
+    tiles (64 x 32 queries over 8192 keys: no causal imbalance);
   * schedule: the prefill of the two large batches under the three issue
     orders (heaviest first, stream order, request order);
   * the decode step, the dequant-placement ablation, the measured achievable
@@ -98,6 +99,8 @@ def main():
                     help="only launch the prefill under the dequant placements (for counters)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (HBM-counter calibration)")
+    ap.add_argument("--steady-only", action="store_true",
+                    help="only launch the 2048x2048 prefill and the steady-state batch (for counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -132,6 +135,14 @@ def main():
     kvp_d, pt_d = kvp_h.to(dev), torch.from_numpy(w.page_table).to(dev)
     out = torch.empty_like(w.q)
 
+    if args.steady_only:
+        cache.append(w.k, w.v, w.slot_mapping)
+        plan = K.plan(qo_h, kvl_h, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size, kv_indptr=kvp_h)
+        for _ in range(60):
+            K.paged_prefill_causal(w.q, qo_d, kvp_d, pt_d, kvl_d, cache, out, w.sm_scale, plan=plan)
+        torch.cuda.synchronize()
+        print(json.dumps({"steady_state": bench_steady(K, W, dev, torch, launches=12)}), flush=True)
+        return
     if args.ablation_only:
         cache.append(w.k, w.v, w.slot_mapping)
         print(json.dumps({"dequant_ablation": bench_dequant_ablation(
@@ -237,6 +248,8 @@ def main():
             "bytes_per_launch": st["bytes_per_launch"], "cold_median_us": st["median_launch_us"],
             "cold_back_to_back_us": st["back_to_back_avg_us"], "frac": st["frac"],
             "frac_back_to_back": st["frac_back_to_back"]}}
+    if not args.no_configs:
+        configs["steady_state_64x32x8192"] = bench_steady(K, W, dev, torch)
     result["configs"] = configs
     if not args.no_decode:
         result["decode"] = bench_decode(K, W, dev, torch, np)
@@ -315,6 +328,31 @@ def bench_config_small(K, W, dev, torch):
             "prefill_bf16": {"dequant_mode": 3, **tflops_row(flops, pre3)},
             "append": {"bytes_per_launch": nbytes, **gbs_row(nbytes, app)},
             "note": "a few microseconds of work: bound by launch latency, not by the roofline"}
+
+
+def bench_steady(K, W, dev, torch, launches=0):
+    """The prefill kernel of the 2048x2048 batch (4-wave tiles, no KV split)
+    on equal-cost tiles: 64 requests x 32 queries over 8192 keys, 512 tiles
+    of 128 KV tiles each, two per CU, so neither causal imbalance nor the
+    prologue weighs.  launches > 0: just that many launches (for counters)."""
+    w = W.steady_state(dev)
+    cache = K.PagedCache.empty(w.num_pages, w.page_size, w.num_kv_heads, w.head_dim, dev,
+                               w.k_scale, w.v_scale)
+    cache.append(w.k, w.v, w.slot_mapping)
+    args = _dev_arrays(w, dev, torch)
+    out = torch.empty_like(w.q)
+    plan = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), w.num_q_heads, w.num_kv_heads,
+                  w.head_dim, w.page_size, kv_indptr=torch.from_numpy(w.kv_indptr), tile_waves=4, split_len=-1)
+    fn = lambda: K.paged_prefill_causal(w.q, *args, cache, out, w.sm_scale, plan=plan)
+    flops = attention_flops(w.q_lens, w.kv_lens, w.num_q_heads, w.head_dim)
+    if launches:
+        for _ in range(launches):
+            fn()
+        torch.cuda.synchronize()
+        return {"workload": w.name, "launches": launches}
+    ms = graph_launch_ms(torch, fn, per_graph=10, replays=5)
+    return {"workload": w.name, "prefill": {"flops_per_launch": flops, "tiles": plan.num_tiles,
+                                            "block_q": plan.block_q, **tflops_row(flops, ms)}}
 
 
 def bench_config_large(K, w, torch, chunk_append=False):

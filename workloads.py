@@ -209,6 +209,15 @@ def ragged_chunked(device="cpu", batch=256) -> AttentionWorkload:
     return w
 
 
+def steady_state(device="cpu", batch=64, q_len=32, kv_len=8192) -> AttentionWorkload:
+    """64 requests x 32 queries at the end of 8192 keys each, 32/8 heads,
+    head_dim 128, page 16, random page table, scales per-tensor amax /
+    (6*448): every 4-wave Q tile visits 128 KV tiles, so the prefill runs
+    equal-cost tiles, two per CU, with a negligible prologue."""
+    return make_attention(f"steady_{batch}x{q_len}x{kv_len}_h32_kv8_d128", [q_len] * batch, [kv_len] * batch,
+                          32, 8, 128, 16, batch * kv_len // 16 + 8, seed=6, device=device, scales="amax")
+
+
 def decode_batch(device="cpu", batch=32, kv_len=8192) -> AttentionWorkload:
     """One decode step: 32 requests x 1 new query token over 8192 cached keys
     each (the token at position kv_len - 1), 32/8 heads, head_dim 128, page
