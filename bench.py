@@ -266,6 +266,8 @@ def main():
     if not args.no_achievable:
         ach = bench_achievable(K, W, dev, torch, np)
         ach["prefill_frac_of_mfma_loop"] = round(pre_tflops / ach["mfma_bf16_TFLOPs"], 4)
+        ach["prefill_frac_of_mfma_loop_random_operands"] = round(
+            pre_tflops / ach["mfma_bf16_random_operands_TFLOPs"], 4)
         if "append_stress" in result:
             got = result["append_stress"]["achieved_GBps"]
             ach["append_stress_frac_of_copy"] = round(got / ach["copy_GBps"], 4)
@@ -553,7 +555,9 @@ def bench_achievable(K, W, dev, torch, np):
     (peak.hip decode_traffic: the same waves, page lookups and per-lane
     loads, with one tile in flight as the decode has, and with two; the
     decode's algorithmic bytes / time).  Warm: the MFMA-only loop of peak.hip
-    (dense v_mfma_f32_32x32x16_bf16, two waves per SIMD; median of 10)."""
+    (dense v_mfma_f32_32x32x16_bf16, two waves per SIMD; median of 10), with
+    smooth operands and with random operand bits (the part's clock depends
+    on them)."""
     import ctypes
     from nvfp4_paged_kv_amd.build import PEAK_LIB
     if not os.path.exists(PEAK_LIB):
@@ -639,6 +643,14 @@ def bench_achievable(K, W, dev, torch, np):
 
     mfma_s = timed(mfma)
     out["mfma_bf16_TFLOPs"] = round(L.nvfp4kv_mfma_peak_probe_flops(blocks, iters) / mfma_s / 1e12, 1)
+    L.nvfp4kv_mfma_random_peak_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+
+    def mfma_random():
+        if L.nvfp4kv_mfma_random_peak_probe(blocks, iters, ctypes.c_void_p(buf.data_ptr()), stream) != 0:
+            raise SystemExit("MFMA peak probe launch failed")
+
+    out["mfma_bf16_random_operands_TFLOPs"] = round(
+        L.nvfp4kv_mfma_peak_probe_flops(blocks, iters) / timed(mfma_random) / 1e12, 1)
     return out
 
 

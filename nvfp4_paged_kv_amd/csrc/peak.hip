@@ -1,6 +1,7 @@
 // peak.hip -- achievable-peak probes for the measurement harness (not part of
 // the hot path): a dense loop of independent v_mfma_f32_32x32x16_bf16 with two
-// waves per SIMD (the rate the matrix cores reach with no memory traffic); a
+// waves per SIMD (the rate the matrix cores reach with no memory traffic, with
+// smooth or with random operand bits); a
 // 16-byte-per-lane device copy; the append's own data movement without its
 // arithmetic (the same bf16 loads, 4-byte code stores and scale-byte stores,
 // scattered through the same slot mapping); and the decode's loads without
@@ -19,13 +20,28 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kAcc = 8;  // independent accumulators per wave
 
+// RANDOM: operands of random sign, exponent and mantissa bits (each lane's
+// own, like real data) instead of smooth ramps: the matrix cores' power, and
+// with it the clock the part holds, depends on the operand bits.
+template <bool RANDOM>
 __global__ __launch_bounds__(512) void mfma_loop(int iters, float* out) {
   const int t = threadIdx.x;
   bf16x8 a, b;
+  uint32_t x = (uint32_t)(blockIdx.x * 512 + t) * 2654435761u + 12345u;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    a[i] = (__bf16)(0.001f * (float)(t + i));
-    b[i] = (__bf16)(0.002f * (float)(t - i));
+    if constexpr (RANDOM) {
+      // bf16 bit patterns with exponents in [2^-4, 2^4): finite, nonzero
+      x = x * 1664525u + 1013904223u;
+      const uint16_t ha = (uint16_t)((x >> 16) & 0x807Fu) | (uint16_t)((123u + ((x >> 8) & 7u)) << 7);
+      x = x * 1664525u + 1013904223u;
+      const uint16_t hb = (uint16_t)((x >> 16) & 0x807Fu) | (uint16_t)((123u + ((x >> 8) & 7u)) << 7);
+      a[i] = __builtin_bit_cast(__bf16, ha);
+      b[i] = __builtin_bit_cast(__bf16, hb);
+    } else {
+      a[i] = (__bf16)(0.001f * (float)(t + i));
+      b[i] = (__bf16)(0.002f * (float)(t - i));
+    }
   }
   f32x16 acc[kAcc];
 #pragma unroll
@@ -225,7 +241,14 @@ extern "C" int nvfp4kv_decode_traffic_probe(const int32_t* kv_indptr, const int3
 // bad argument or launch error.
 extern "C" int nvfp4kv_mfma_peak_probe(int blocks, int iters, float* out, void* stream) {
   if (blocks <= 0 || iters <= 0 || !out) return -1;
-  hipLaunchKernelGGL(mfma_loop, dim3(blocks), dim3(512), 0, (hipStream_t)stream, iters, out);
+  hipLaunchKernelGGL(mfma_loop<false>, dim3(blocks), dim3(512), 0, (hipStream_t)stream, iters, out);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// The same loop with random operand bits (see mfma_loop).
+extern "C" int nvfp4kv_mfma_random_peak_probe(int blocks, int iters, float* out, void* stream) {
+  if (blocks <= 0 || iters <= 0 || !out) return -1;
+  hipLaunchKernelGGL(mfma_loop<true>, dim3(blocks), dim3(512), 0, (hipStream_t)stream, iters, out);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
