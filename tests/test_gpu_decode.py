@@ -81,6 +81,28 @@ def test_decode_every_heads_per_wave_kernel(K, oracle, hq, hk, d, hp):
     print(f"max err {e:.3g}")
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_decode_random_shapes(K, oracle, seed):
+    """Seeded random decode batches against the oracle: 1-9 requests of 1-700
+    keys, 1/2/3/4/8 KV heads, GQA group 1/2/4/8, head_dim 64/128, page sizes
+    that do and do not divide a tile, automatic or forced chunk lengths (so
+    every heads-per-wave kernel meets ragged lengths and several chunks)."""
+    r = np.random.default_rng(1000 + seed)
+    B = int(r.integers(1, 10))
+    hk = int(r.choice([1, 2, 3, 4, 8]))
+    g = int(r.choice([1, 2, 4, 8]))
+    d = int(r.choice([64, 128]))
+    ps = int(r.choice([1, 5, 16, 32, 64]))
+    chunk = int(r.choice([0, 64, 128, 192]))
+    kv = [int(x) for x in r.integers(1, 701, B)]
+    pool = sum((k + ps - 1) // ps for k in kv) + 3
+    banner(f"decode random shape {seed}: B={B} hk={hk} G={g} d={d} page={ps} chunk={chunk} kv={kv}")
+    w = W.make_attention(f"decode_rand_{seed}", [1] * B, kv, hk * g, hk, d, ps, pool, seed=60 + seed,
+                         device="cuda", scales="amax")
+    e, plan = _check(K, oracle, w, chunk_len=chunk)
+    print(f"max err {e:.3g}; heads per wave {plan.heads_per_wave}, chunks {plan.max_chunks}")
+
+
 @pytest.mark.parametrize("chunk_len", [64, 128, 192, 1024])
 def test_decode_forced_chunks(K, oracle, chunk_len):
     """Chunks merged in order: one tile per chunk, uneven last chunks,
