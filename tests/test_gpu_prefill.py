@@ -146,6 +146,38 @@ def test_prefill_ragged_chunked_sampled(K, oracle):
     print(f"max err {e:.3g}")
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_prefill_random_shapes(K, oracle, seed):
+    """Seeded random batches against the oracle: 1-6 requests of 1-600 keys
+    with 0..kv_len queries each, 1/2/3/4/8 KV heads, GQA group 1/2/4/8,
+    head_dim 64/128, page sizes that do and do not divide a tile, 4- or
+    8-wave tiles (head_dim 128), no / automatic / forced KV splits, f16 or
+    bf16 staging."""
+    r = np.random.default_rng(2000 + seed)
+    B = int(r.integers(1, 7))
+    hk = int(r.choice([1, 2, 3, 4, 8]))
+    g = int(r.choice([1, 2, 4, 8]))
+    d = int(r.choice([64, 128]))
+    ps = int(r.choice([1, 5, 16, 32, 64]))
+    waves = int(r.choice([4, 8])) if d == 128 else 4
+    split = int(r.choice([-1, 0, 2, 3]))
+    mode = int(r.choice([0, 3]))
+    kv = [int(x) for x in r.integers(1, 601, B)]
+    q = [int(r.integers(0, k + 1)) if r.random() < 0.8 else k for k in kv]
+    if sum(q) == 0:
+        q[0] = kv[0]
+    pool = sum((k + ps - 1) // ps for k in kv) + 3
+    banner(f"prefill random shape {seed}: hk={hk} G={g} d={d} page={ps} waves={waves} split={split} "
+           f"mode={mode} q={q} kv={kv}")
+    w = W.make_attention(f"prefill_rand_{seed}", q, kv, hk * g, hk, d, ps, pool, seed=80 + seed,
+                         device="cuda", scales="amax")
+    plan = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), w.num_q_heads, w.num_kv_heads,
+                  w.head_dim, w.page_size, kv_indptr=torch.from_numpy(w.kv_indptr), split_len=split,
+                  tile_waves=waves, dequant_mode=mode)
+    e, _, plan = _check(K, oracle, w, plan=plan)
+    print(f"max err {e:.3g}; tiles {plan.num_tiles}, split {plan.split_len}, chunks {plan.max_chunks}")
+
+
 def test_schedule_orders_give_identical_bits(K):
     """Uniform O(1) decode and the device work list, each in the three issue
     orders (heaviest first, stream order, request order), and split Q tiles
