@@ -157,6 +157,41 @@ def test_zero_rows_launch_nothing_and_check_nothing(K):
     assert K.read_device_error(word=err) == 0
 
 
+@pytest.mark.parametrize("seed", range(16))
+def test_append_random_shapes(K, oracle, seed):
+    """Seeded random appends, whole caches compared byte for byte: 1-700
+    tokens, 1/2/3/5/8 KV heads, head_dim 16/48/64/128, page sizes 1/5/16/64,
+    values N(0, s) with s spanning 2^-20 .. 2^20 and some exact zeros, a few
+    padding (-1) and out-of-range slots, global scales of either kind."""
+    r = np.random.default_rng(3000 + seed)
+    T = int(r.integers(1, 701))
+    H = int(r.choice([1, 2, 3, 5, 8]))
+    D = int(r.choice([16, 48, 64, 128]))
+    ps = int(r.choice([1, 5, 16, 64]))
+    P = (T + ps - 1) // ps + int(r.integers(1, 6))
+    g = torch.Generator().manual_seed(3000 + seed)
+    scale = 2.0 ** float(r.uniform(-20, 20))
+    k = (torch.randn(T, H, D, generator=g) * scale).to(torch.bfloat16)
+    v = (torch.randn(T, H, D, generator=g) * scale * 7).to(torch.bfloat16)
+    k[torch.rand(T, H, D, generator=g) < 0.05] = 0.0
+    slots = torch.randperm(P * ps, generator=g)[:T].to(torch.int64)
+    n_bad = int(r.integers(0, 4))
+    if n_bad:
+        idx = torch.from_numpy(r.choice(T, size=min(n_bad, T), replace=False))
+        slots[idx[: len(idx) // 2 + 1]] = -1
+        slots[idx[len(idx) // 2 + 1:]] = P * ps + int(r.integers(0, 100))
+    ks, vs = (1.0, 1.0) if r.random() < 0.3 else (float(scale * r.uniform(0.01, 1)) / 2688.0,
+                                                    float(scale * 7 * r.uniform(0.01, 1)) / 2688.0)
+    banner(f"append random shape {seed}: T={T} H={H} D={D} page={ps} P={P} scale={scale:.3g} bad slots {n_bad}")
+    k, v, slots = k.cuda(), v.cuda(), slots.cuda()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cache = _gpu_append(K, k, v, slots, ks, vs, P, ps, err)
+    ref, oerr = _oracle_cache(oracle, k, v, slots, ks, vs, P, ps)
+    got_bits = K.read_device_error(word=err)
+    assert got_bits == oerr
+    _compare(cache, ref)
+
+
 def test_padding_and_out_of_range_slots(K, oracle):
     w = W.tiny("cuda")
     slots = w.slot_mapping.clone()
