@@ -44,6 +44,7 @@ sys.path.insert(0, ROOT)
 METRIC = "causal prefill TFLOP/s + append GB/s on NVFP4 paged KV (% of MI355X roofline)"
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 (= f16) MFMA, TFLOP/s
+SCHEDULE_NAMES = {1: "heaviest_first", 2: "stream_order", 3: "request_order", 4: "paired"}
 PREFILL_TARGET_FRAC = 0.40  # of the MFMA peak, on the 2048x2048 prefill
 APPEND_TARGET_FRAC = 0.70   # of HBM bandwidth, on the 65,536-token append
 SETTLE_MS = 60.0
@@ -193,7 +194,9 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     pre_tflops = flops / (pre_ms * 1e-3) / 1e12
     G = w.num_q_heads // w.num_kv_heads
-    kernel_name = f"prefill_kernel<{w.head_dim},{G},{plan.block_q * G // 32},{'true' if 64 % w.page_size == 0 else 'false'},0>"
+    paired = plan.schedule == K.SCHEDULE_PAIRED
+    kernel_name = (f"prefill_kernel<{w.head_dim},{G},{plan.block_q * G // 32},"
+                   f"{'true' if 64 % w.page_size == 0 else 'false'},0,{'true' if paired else 'false'}>")
     traffic = _traffic("prefill_2k")
     frac = pre_tflops / BF16_PEAK_TFLOPS
     result = {
@@ -217,7 +220,7 @@ def main():
                               "dequant_mode 3: configs.*.prefill_bf16)",
                    "step": "append 2048 K/V rows + causal paged prefill",
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": kernel_name,
+        "roofline": {"bound": "mfma", "kernel": kernel_name, "schedule": SCHEDULE_NAMES[plan.schedule],
                      "achieved": round(pre_tflops, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(frac, 4),
                      "traffic": traffic, "flops_per_launch": flops,
@@ -233,6 +236,21 @@ def main():
         configs["small_2x128"] = bench_config_small(K, W, dev, torch)
     configs["prefill_2k"] = {"workload": w.name, "prefill": {"flops_per_launch": flops, **tflops_row(flops, pre_ms)},
                              "append": {"bytes_per_launch": abytes, **gbs_row(abytes, app_ms)}}
+    if not args.no_configs:
+        # the same prefill under heaviest-first and paired issue (bitwise the
+        # same outputs), interleaved
+        sched = {}
+        for rep in range(2):
+            for name, s in (("heaviest_first", K.SCHEDULE_HEAVIEST), ("paired", K.SCHEDULE_PAIRED)):
+                p = K.plan(qo_h, kvl_h, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                           kv_indptr=kvp_h, schedule=s)
+                ms = graph_launch_ms(torch, lambda: K.paged_prefill_causal(w.q, qo_d, kvp_d, pt_d, kvl_d, cache,
+                                                                           out, w.sm_scale, plan=p))
+                if rep == 1:
+                    sched[name] = tflops_row(flops, ms)
+        sched["paired_speedup"] = round(sched["heaviest_first"]["avg_launch_us"] / sched["paired"]["avg_launch_us"], 3)
+        sched["plan_choice"] = SCHEDULE_NAMES[plan.schedule]
+        configs["prefill_2k"]["schedule"] = sched
     del cache, out
     if not args.no_configs:
         configs["uniform_1024x1024"], result["schedule_uniform_1024x1024"] = bench_config_large(
@@ -407,7 +425,7 @@ def bench_config_large(K, w, torch, chunk_append=False):
     base = sched["request_order"]["avg_launch_us"]
     for name in ("heaviest_first", "stream_order"):
         sched[name]["speedup_vs_request_order"] = round(base / sched[name]["avg_launch_us"], 3)
-    sched["plan_choice"] = {1: "heaviest_first", 2: "stream_order", 3: "request_order"}[plan.schedule]
+    sched["plan_choice"] = SCHEDULE_NAMES[plan.schedule]
     bits = K.read_device_error(dev)
     if bits:
         raise SystemExit(f"device error bits {bits} on {w.name}")

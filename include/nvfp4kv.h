@@ -132,7 +132,9 @@ typedef struct {
   int64_t workspace_bytes;  /* device workspace paged_prefill_causal needs */
   int32_t split_len;        /* KV tiles per chunk of a split Q tile (0: no split) */
   int32_t max_chunks;       /* chunks of the most split Q tile */
-  int64_t num_items;        /* workgroups launched: Q tiles, or their KV chunks */
+  int64_t num_items;        /* work items: Q tiles, or their KV chunks (one
+                               workgroup each; under schedule 4 two Q tiles
+                               share one workgroup) */
   int64_t num_split_tiles;  /* Q tiles (x KV heads) whose KV range is split */
   /* Dequant-placement ablation (the PR #4769 page's before/after comparison);
      the plan sets 0 and a caller may change it before paged_prefill_causal:
@@ -174,8 +176,19 @@ typedef struct {
           not fit in L2, [PR #3575] section 3); not with split Q tiles, and
           for ragged batches only with num_kv_heads % 8 == 0 and batch <= 8192;
        3  request order: requests in order, each one's Q tiles lightest first
-          (no reordering; the baseline the other two are measured against).
-     Other values, or 2 where it is not available, return
+          (no reordering; the baseline the others are measured against);
+       4  paired order: Q tiles t and q_tiles_per_head - 1 - t of one
+          (request, KV head) -- together about the same number of KV tiles
+          for every t ([PR #3575] section 2 balances causal tiles by issuing
+          the heavy ones first; here each heavy tile is matched with a light
+          one) -- share one workgroup of twice the tile's waves: the light
+          tile's waves stage every KV tile of the pair (the heavy tile's
+          range) and compute their own, the heavy tile's waves only
+          compute.  The plan's choice for uniform batches of 4-wave tiles
+          that fill every workgroup slot without a split and whose KV fits
+          in L2; available for uniform batches (uniform_q) of 4-wave tiles
+          (block_q x G == 128) with nothing split (split_len 0).
+     Other values, or 2 or 4 where it is not available, return
      NVFP4KV_EUNSUPPORTED. */
   int32_t schedule;
 } nvfp4kv_prefill_plan;

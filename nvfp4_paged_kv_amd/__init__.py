@@ -332,7 +332,7 @@ def _host_int32(t, name) -> torch.Tensor:
     return t.to(torch.int32).contiguous()
 
 
-SCHEDULE_HEAVIEST, SCHEDULE_STREAM, SCHEDULE_REQUEST = 1, 2, 3
+SCHEDULE_HEAVIEST, SCHEDULE_STREAM, SCHEDULE_REQUEST, SCHEDULE_PAIRED = 1, 2, 3, 4
 
 
 def plan(qo_indptr, kv_lens, num_q_heads, num_kv_heads, head_dim, page_size, kv_indptr=None,
@@ -348,7 +348,9 @@ def plan(qo_indptr, kv_lens, num_q_heads, num_kv_heads, head_dim, page_size, kv_
     MX scores -- MXFP4 (4) or MXFP8 (5) keys, MXFP8 queries, the scaled
     matrix instruction, under looser accuracy contracts); schedule: issue
     order of the Q tiles (0: the plan's choice; SCHEDULE_HEAVIEST,
-    SCHEDULE_STREAM or SCHEDULE_REQUEST)."""
+    SCHEDULE_STREAM, SCHEDULE_REQUEST, or SCHEDULE_PAIRED -- Q tiles t and
+    QT - 1 - t of a uniform, unsplit batch of 4-wave tiles in one 8-wave
+    workgroup)."""
     return Plan(qo_indptr, kv_lens, num_q_heads, num_kv_heads, head_dim, page_size, kv_indptr,
                 l2_bytes, split_len, tile_waves, dequant_mode, cu_count, schedule)
 

@@ -21,20 +21,24 @@ LIB = os.path.join(PKG, "libnvfp4kv.so")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
-SOURCES = {
-    "append.hip": ["-ffp-contract=off"],
-    "prefill.hip": [],
-    "decode.hip": [],
-    "host.cpp": ["-x", "hip"],
-}
+# (source, object, extra flags): the prefill source is compiled as three
+# shards (each instantiates a third of the kernels; compiled in parallel)
+SOURCES = [
+    ("append.hip", "append", ["-ffp-contract=off"]),
+    ("prefill.hip", "prefill_0", ["-DNVFP4KV_PREFILL_SHARD=0"]),
+    ("prefill.hip", "prefill_1", ["-DNVFP4KV_PREFILL_SHARD=1"]),
+    ("prefill.hip", "prefill_2", ["-DNVFP4KV_PREFILL_SHARD=2"]),
+    ("decode.hip", "decode", []),
+    ("host.cpp", "host", ["-x", "hip"]),
+]
 
 
 def _hipcc():
     return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
-def _compile(src, extra, defines):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src, name, extra, defines):
+    obj = os.path.join(BUILD, name + ".o")
     cmd = [_hipcc(), *COMMON, *extra, *defines, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -46,7 +50,7 @@ def build(out: str = LIB, defines=()) -> str:
     """Compile every source and link the shared library; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(lambda kv: _compile(kv[0], kv[1], list(defines)), SOURCES.items()))
+        objs = list(ex.map(lambda e: _compile(e[0], e[1], e[2], list(defines)), SOURCES))
     tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

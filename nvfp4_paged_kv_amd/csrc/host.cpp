@@ -165,6 +165,12 @@ extern "C" int nvfp4_prefill_plan(const int32_t* qo_indptr_host, const int32_t* 
   // otherwise stream order (each stream's KV fetched once into one XCD's L2)
   // where it is available, else heaviest first.
   p.schedule = !p.head_first && stream_order_available(p) ? kOrderStream : kOrderHeaviest;
+  // Paired order instead of heaviest first for uniform batches of 4-wave
+  // tiles that fill every workgroup slot without a split: the heavy causal
+  // tiles, which set the batch's length, run with their staging done by the
+  // waves of their light partners.
+  if (p.schedule == kOrderHeaviest && paired_order_available(p) && p.num_tiles >= slots)
+    p.schedule = kOrderPaired;
   // Ragged or split batches need a device work list (and, when split, the
   // chunks' partials and arrival counters).
   p.workspace_bytes = workspace_layout(p).total;
@@ -247,4 +253,4 @@ extern "C" const char* nvfp4kv_status_string(int status) {
   }
 }
 
-extern "C" int nvfp4kv_abi_version(void) { return 103; }
+extern "C" int nvfp4kv_abi_version(void) { return 104; }

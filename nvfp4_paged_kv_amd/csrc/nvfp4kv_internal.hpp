@@ -35,12 +35,20 @@ constexpr int kMaxChunks = 16;
 constexpr int kOrderHeaviest = 1;
 constexpr int kOrderStream = 2;
 constexpr int kOrderRequest = 3;
+constexpr int kOrderPaired = 4;
 constexpr int kXcds = 8;
 constexpr int kStreamOrderMaxReq = 8192;
 inline bool stream_order_available(const nvfp4kv_prefill_plan& p) {
   const bool list = !p.uniform_q || p.split_len > 0;
   return p.split_len == 0 &&
          (!list || (p.num_kv_heads % kXcds == 0 && p.batch <= kStreamOrderMaxReq));
+}
+
+// Paired order: uniform batches of 4-wave tiles with nothing split (no work
+// list): Q tiles pp and q_tiles_per_head - 1 - pp of one (request, KV head)
+// share one 8-wave workgroup.
+inline bool paired_order_available(const nvfp4kv_prefill_plan& p) {
+  return p.uniform_q && p.split_len == 0 && p.block_q * (p.num_q_heads / p.num_kv_heads) == 128;
 }
 
 // Workspace layout of one prefill call (shared by the plan and the launcher):

@@ -38,17 +38,25 @@
 #include "nvfp4kv_codec.hpp"
 #include "nvfp4kv_internal.hpp"
 
-namespace nvfp4kv {
-namespace {
+#ifndef NVFP4KV_PREFILL_SHARD
+#define NVFP4KV_PREFILL_SHARD 0
+#endif
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+namespace nvfp4kv {
+
+// Arguments of one prefill launch (the kernels' only parameter).
+struct PrefillArgs;
+
+// The kernel templates below are compiled in three translation units (this
+// file built once per shard, the shards in parallel): shard k instantiates
+// the kernels prefill_shard_of assigns it and exports
+// launch_prefill_shard<k>, which launches the kernel of a shape if it holds
+// it; shard 0 also holds the work-list kernel, the C entry points and the
+// no-allocation scratch array.
+constexpr int prefill_shard_of(int head_dim, bool paired) { return head_dim == 64 ? 2 : paired ? 1 : 0; }
+bool launch_prefill_shard0(const PrefillArgs& a, int D, int G, int W, int dq, bool paired, hipStream_t s);
+bool launch_prefill_shard1(const PrefillArgs& a, int D, int G, int W, int dq, bool paired, hipStream_t s);
+bool launch_prefill_shard2(const PrefillArgs& a, int D, int G, int W, int dq, bool paired, hipStream_t s);
 
 struct PrefillArgs {
   const uint16_t* q;
@@ -77,6 +85,18 @@ struct PrefillArgs {
   int snake;  // every tile is resident at once: pair heavy with light tiles
   uint32_t num_tiles, num_items;
 };
+
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 
 template <int D, int G, int W>
 struct Cfg {
@@ -304,9 +324,10 @@ __device__ __forceinline__ int mx8_exponent_of_scale(float smax) {
 // exact multiplication by 2^-e.  Byte c of the returned word is e + 127 of
 // block (c, hh), the one this lane's scale operand carries; sh goes into
 // *cmul as 2^sh.
-// (DQ only gives each kernel its own instance: the host pass of this compiler
-// rejects a second kernel's call to a shared instance of this function)
-template <int DQ, int NC>
+// (DQ and TAG only give each kernel its own instance: the host pass of this
+// compiler rejects a second kernel's call to a shared instance of this
+// function)
+template <int DQ, int TAG, int NC>
 __device__ __forceinline__ uint32_t load_q_mx(const uint16_t* qrow, int hh, i32x8 (&q8)[NC], float& cmul) {
   u32x4 qw[NC][4];
   uint32_t bm[NC][2];  // largest |bf16| bit pattern of each MX block (t: chunk 2hh + t, block t)
@@ -607,6 +628,19 @@ struct TileStager {
   }
 };
 
+// The stand-in of a wave that stages nothing (the heavy half of a pair):
+// no state, no loads, no LDS writes.
+struct NoStager {
+  template <class J>
+  __device__ __forceinline__ NoStager(const J*, bool, uint8_t*, int) {}
+  template <int P, class J>
+  __device__ __forceinline__ void piece(const J*) {}
+};
+template <bool STAGE, int D, int G, int W, int DQ>
+struct StagerOf {
+  using type = typename std::conditional<STAGE, TileStager<D, G, W, DQ>, NoStager>::type;
+};
+
 // The work item of workgroup `tile`: request b, KV head hk, Q tile qt, and
 // the KV tile range [jt_begin, jt_end) (the whole range unless the item is
 // one chunk of a split Q tile; split: -1, or (split id << 10) | (chunk << 5)
@@ -614,6 +648,27 @@ struct TileStager {
 struct Item {
   int b, hk, qt, jt_begin, jt_end, split;
 };
+
+// Paired order: work item `tile` is the pair pp of (request, KV head) bh --
+// its Q tile pp (the light one) and QT - 1 - pp (the heavy one), which see
+// about the same number of KV tiles together whatever pp is.  The light
+// tile's waves also stage every KV tile the heavy one visits.  The middle
+// tile of an odd count has no partner: its light half holds no rows (qt =
+// QT).  Returns this half's item; `qt_heavy` is the tile whose keys the
+// staging covers.
+__device__ __forceinline__ Item decode_pair(const PrefillArgs& a, uint32_t tile, bool heavy, int& qt_heavy) {
+  Item it;
+  it.jt_begin = 0;
+  it.jt_end = 0x7FFFFFFF;
+  it.split = -1;
+  const uint32_t bh_n = (uint32_t)a.B * a.Hk;
+  const uint32_t pp = tile / bh_n, bh = tile - pp * bh_n;
+  it.b = bh / a.Hk;
+  it.hk = bh - it.b * a.Hk;
+  qt_heavy = a.QT - 1 - (int)pp;
+  it.qt = heavy ? qt_heavy : ((int)pp < qt_heavy ? (int)pp : a.QT);
+  return it;
+}
 __device__ __forceinline__ Item decode_item(const PrefillArgs& a, uint32_t tile) {
   Item it;
   it.jt_begin = 0;
@@ -800,17 +855,27 @@ __device__ __forceinline__ bool split_merge(const PrefillArgs& a, int split, int
   return true;
 }
 
-template <int D, int G, int W, bool PA, int DQ>
-__global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
+// PAIR: two W-wave tiles in one workgroup of 2W waves (the paired order):
+// waves [0, W) compute the light Q tile and stage every KV tile of the pair,
+// waves [W, 2W) compute the heavy one and stage nothing, so that the tile
+// on the longest path runs its matrix and softmax work with the staging on
+// the other waves of its SIMDs.  Every wave passes the same barriers: one
+// after the prologue and one per KV tile of the heavy tile.
+template <int D, int G, int W, bool PA, int DQ, bool PAIR = false>
+__global__ __launch_bounds__(64 * W * (PAIR ? 2 : 1), 8 / (W * (PAIR ? 2 : 1))) void prefill_kernel(PrefillArgs a) {
   using C = Cfg<D, G, W>;
   // Two staging buffers: tile j+1 is dequantized into one while tile j is
   // read from the other, with a single barrier per KV tile.
   constexpr int STG = C::K_STAGE + C::V_STAGE;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STG];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid_all = threadIdx.x, lane = tid_all & 63;
+  const bool heavy = PAIR && tid_all >= C::NT;  // (wave-uniform)
+  const int tid = PAIR ? tid_all & (C::NT - 1) : tid_all;  // thread within this half
+  const int wave = tid >> 6;
   const int n = lane & 31, hh = lane >> 5;
 
-  const Item it = decode_item(a, blockIdx.x);
+  int qt_stage = 0;
+  const Item it = PAIR ? decode_pair(a, blockIdx.x, heavy, qt_stage) : decode_item(a, blockIdx.x);
   const int b = it.b, hk = it.hk, qt = it.qt, jt_begin = it.jt_begin, jt_end = it.jt_end, split = it.split;
   const uint32_t tile = blockIdx.x;
   const int q_begin = a.qo[b];
@@ -819,19 +884,27 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   const int off = Lk - Lq;  // bottom-right causal alignment
   const int q0 = qt * C::BQ;
   const int rows_valid = min(C::BQ, Lq - q0);
-  if (rows_valid <= 0) return;  // (uniform batches with short requests)
+  if (!PAIR && rows_valid <= 0) return;  // (uniform batches with short requests)
   const int kend_max = off + q0 + rows_valid - 1;  // last key any row sees
   const int kend_min = off + q0;                   // last key of the first row
-  const int ntiles = min(kend_max / C::BN + 1, jt_end);  // this workgroup's KV tiles: [jt_begin, ntiles)
+  // this half's KV tiles: [jt_begin, ntiles) (none for a half without rows)
+  const int ntiles = rows_valid > 0 ? min(kend_max / C::BN + 1, jt_end) : jt_begin;
+  // the keys the staging covers: the heavy tile's when paired
+  const int kend_stage = PAIR ? off + qt_stage * C::BQ + min(C::BQ, Lq - qt_stage * C::BQ) - 1 : kend_max;
+  const int nstage = PAIR ? kend_stage / C::BN + 1 : ntiles;
   const int32_t* ptb = a.pt + a.kvp[b];
 
   // Software pipeline: data of tile jt+1 and the page id of tile jt+2 are in
   // flight while tile jt is computed.
   RawJob<D> job[C::JOBS_PER_THREAD];
   bool page_bad = false;
-  const KeyAddr<D, G, W, PA> ka(a, tid, hk, kend_max, ptb);
-  bool live = ka.load(a, job, jt_begin, ka.lookup(a, jt_begin), page_bad);
-  int page_next = ka.lookup(a, jt_begin + 1);
+  const KeyAddr<D, G, W, PA> ka(a, tid, hk, kend_stage, ptb);
+  bool live = false;
+  int page_next = 0;
+  if (!heavy) {
+    live = ka.load(a, job, jt_begin, ka.lookup(a, jt_begin), page_bad);
+    page_next = ka.lookup(a, jt_begin + 1);
+  }
 
   const int r = wave * 32 + n;  // this lane's tile row
   const int tr = r % C::BQ, g = r / C::BQ;
@@ -841,16 +914,18 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   const int kend = off + tok;
 
   const float gk = *a.kscale, gv = *a.vscale;
-  if (tile == 0 && tid == 0 && !(scale_ok(gk) && scale_ok(gv)))
+  if (tile == 0 && tid_all == 0 && !(scale_ok(gk) && scale_ok(gv)))
     atomicOr(a.err, (uint32_t)NVFP4KV_DEV_BAD_SCALE_ATTN);
-  const uint16_t* const qrow = a.q + ((int64_t)(q_begin + (row_valid ? tok : q0)) * a.Hq + hq) * D;
+  // (rows past the tile's end read the tile's first row; a paired light half
+  // without rows reads the request's first)
+  const uint16_t* const qrow = a.q + ((int64_t)(q_begin + (row_valid ? tok : rows_valid > 0 ? q0 : 0)) * a.Hq + hq) * D;
   f16x8 qf[C::NDC];    // 16-bit Q^T fragments (modes 0-3)
   i32x8 q8[D / 64];    // MXFP8 Q^T fragments (modes 4, 5)
   uint32_t qsc = 0;    // their E8M0 scale bytes, one per K-step
   float cscale;
   if constexpr (DQ >= 4) {
     float cmul;
-    qsc = load_q_mx<DQ>(qrow, hh, q8, cmul);
+    qsc = load_q_mx<DQ, PAIR ? 1 : 0>(qrow, hh, q8, cmul);
     cscale = a.sm_scale_log2 * gk * cmul;
   } else {
     cscale = load_q<D, DQ>(qrow, hh, a.sm_scale_log2 * gk, qf);
@@ -871,24 +946,27 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
 
   // Pipeline prologue: the first tile staged (into buffer jt_begin & 1), the
   // next tile's NVFP4 bytes and the one after's page ids in flight.
-  pin_jobs<D, G, W>(job);
-  {
-    TileStager<D, G, W, DQ> st(job, live, smem + (jt_begin & 1) * STG, tid);
-    static_for<0, TileStager<D, G, W, DQ>::PIECES>([&](auto pc) { st.template piece<decltype(pc)::value>(job); });
+  if (!heavy) {
+    pin_jobs<D, G, W>(job);
+    {
+      TileStager<D, G, W, DQ> st(job, live, smem + (jt_begin & 1) * STG, tid);
+      static_for<0, TileStager<D, G, W, DQ>::PIECES>([&](auto pc) { st.template piece<decltype(pc)::value>(job); });
+    }
+    live = ka.load(a, job, jt_begin + 1, page_next, page_bad);
+    page_next = ka.lookup(a, jt_begin + 2);
   }
-  live = ka.load(a, job, jt_begin + 1, page_next, page_bad);
-  page_next = ka.lookup(a, jt_begin + 2);
   __syncthreads();
 
   // One KV tile j: S^T = K Q^T from buffer j&1; dequantize tile j+1 into the
   // other buffer (VALU work that runs beside the matrix cores); prefetch tile
   // j+2; (mask), online softmax, O^T += V^T P^T; one barrier.
-  auto tile_step = [&](const int jt, auto masked, auto exact_form) {
+  auto tile_step = [&](const int jt, auto masked, auto exact_form, auto stage_form) {
     constexpr bool MASK = decltype(masked)::value;
     constexpr bool EXACT = decltype(exact_form)::value;
+    constexpr bool STAGE = decltype(stage_form)::value;  // this wave stages tile j+1
     const uint8_t* const sK = smem + (jt & 1) * STG;
     const uint8_t* const vbase = sK + voff;
-    pin_jobs<D, G, W>(job);
+    if constexpr (STAGE) pin_jobs<D, G, W>(job);
 
     // ---- S^T = K Q^T for 64 keys: lane holds S^T[key 32kb + 8(i/4) + 4hh + i%4][row n].
     // The 2*NDC matrix instructions alternate the two 32-key blocks (no
@@ -919,14 +997,14 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
           kf[2 * c + kb] = (i32x8){(int)v[0], (int)v[1], (int)v[2], (int)v[3], (int)v2[0], (int)v2[1], (int)v2[2], (int)v2[3]};
         }
       }
-      TileStager<D, G, W, DQ> stager(job, live, smem + ((jt + 1) & 1) * STG, tid);
+      typename StagerOf<STAGE, D, G, W, DQ>::type stager(job, live, smem + ((jt + 1) & 1) * STG, tid);
       static_for<0, NQK>([&](auto ic) {
         constexpr int i = decltype(ic)::value, kb = i & 1, c = i >> 1;
         s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[i], q8[c], s[kb], X::FP8 ? 0 : 4, 0, c, ksc[kb], c, qsc);
         constexpr int HP = TileStager<D, G, W, DQ>::PIECES;
         constexpr int P0 = (i * HP + NQK - 1) / NQK, P1 = ((i + 1) * HP + NQK - 1) / NQK;
-        static_for<P0, P1>([&](auto pc) { stager.template piece<decltype(pc)::value>(job); });
-        if constexpr (i == NQK - 1) {
+        if constexpr (STAGE) static_for<P0, P1>([&](auto pc) { stager.template piece<decltype(pc)::value>(job); });
+        if constexpr (STAGE && i == NQK - 1) {
           live = ka.load(a, job, jt + 2, page_next, page_bad);
           page_next = ka.lookup(a, jt + 3);
         }
@@ -953,7 +1031,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
     };
 #pragma unroll
     for (int i = 0; i < KA; ++i) kf[i] = kread(i);
-    TileStager<D, G, W, DQ> stager(job, live, smem + ((jt + 1) & 1) * STG, tid);
+    typename StagerOf<STAGE, D, G, W, DQ>::type stager(job, live, smem + ((jt + 1) & 1) * STG, tid);
     static_for<0, NQK>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       s[i & 1] = mma16<DQ>(kf[i % KA], qf[i >> 1], s[i & 1]);
@@ -961,8 +1039,8 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
       // staging pieces [P0, P1) in this slot
       constexpr int HP = TileStager<D, G, W, DQ>::PIECES;
       constexpr int P0 = (i * HP + NQK - 1) / NQK, P1 = ((i + 1) * HP + NQK - 1) / NQK;
-      static_for<P0, P1>([&](auto pc) { stager.template piece<decltype(pc)::value>(job); });
-      if constexpr (i == NQK - 1) {
+      if constexpr (STAGE) static_for<P0, P1>([&](auto pc) { stager.template piece<decltype(pc)::value>(job); });
+      if constexpr (STAGE && i == NQK - 1) {
         // past the last tile this stages and loads unused (clamped) data
         live = ka.load(a, job, jt + 2, page_next, page_bad);
         page_next = ka.lookup(a, jt + 3);
@@ -1070,16 +1148,23 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
   };
   // KV tiles entirely at or below the first row's last key need no mask.
   const int n_full = min(ntiles, (kend_min + 1) / C::BN);
-  auto kv_loop = [&](auto exact_form) {
+  auto kv_loop = [&](auto exact_form, auto stage_form) {
     int jt = jt_begin;
-    for (; jt < n_full; ++jt) tile_step(jt, std::false_type{}, exact_form);
-    for (; jt < ntiles; ++jt) tile_step(jt, std::true_type{}, exact_form);
+    for (; jt < n_full; ++jt) tile_step(jt, std::false_type{}, exact_form, stage_form);
+    for (; jt < ntiles; ++jt) tile_step(jt, std::true_type{}, exact_form, stage_form);
   };
-  if (exact)
-    kv_loop(std::true_type{});
-  else
-    kv_loop(std::false_type{});
-  if (page_bad) atomicOr(a.err, (uint32_t)NVFP4KV_DEV_PAGE_OOB);
+  if (heavy) {
+    if (exact)
+      kv_loop(std::true_type{}, std::false_type{});
+    else
+      kv_loop(std::false_type{}, std::false_type{});
+  } else {
+    if (exact)
+      kv_loop(std::true_type{}, std::true_type{});
+    else
+      kv_loop(std::false_type{}, std::true_type{});
+  }
+  if (!PAIR && page_bad) atomicOr(a.err, (uint32_t)NVFP4KV_DEV_PAGE_OOB);
 
   float l_tot = l_run + __shfl_xor(l_run, 32);
   if (split >= 0 && !split_merge<D, 32 * W>(a, split, tid, tid, true, r, exact, cscale, m_run, l_tot, o)) return;
@@ -1103,8 +1188,24 @@ __global__ __launch_bounds__(64 * W, 8 / W) void prefill_kernel(PrefillArgs a) {
         *(uint2*)(orow + d) = make_uint2(u0 | ((uint32_t)u1 << 16), u2 | ((uint32_t)u3 << 16));
       }
   }
+  if constexpr (PAIR) {
+    // the light half, its own tiles done, stages the rest of the heavy
+    // tile's KV tiles (one barrier each, as the heavy half's tile steps)
+    if (!heavy) {
+      for (int jt = ntiles; jt < nstage; ++jt) {
+        pin_jobs<D, G, W>(job);
+        TileStager<D, G, W, DQ> st(job, live, smem + ((jt + 1) & 1) * STG, tid);
+        static_for<0, TileStager<D, G, W, DQ>::PIECES>([&](auto pc) { st.template piece<decltype(pc)::value>(job); });
+        live = ka.load(a, job, jt + 2, page_next, page_bad);
+        page_next = ka.lookup(a, jt + 3);
+        __syncthreads();
+      }
+      if (page_bad) atomicOr(a.err, (uint32_t)NVFP4KV_DEV_PAGE_OOB);
+    }
+  }
 }
 
+#if NVFP4KV_PREFILL_SHARD == 0
 // ---- device-built work list (ragged or split batches), heaviest item first.
 // One workgroup: histogram of item costs (KV tiles an item visits), an
 // exclusive scan in descending cost order, then each (request, Q tile) pair,
@@ -1327,17 +1428,85 @@ __global__ __launch_bounds__(1024) void worklist_kernel(const int32_t* __restric
   }
 }
 
-template <int D, int G, int W, int DQ>
+#endif  // NVFP4KV_PREFILL_SHARD == 0
+
+// One launch: a.num_items workgroups of one W-wave tile, or (PAIR, 4-wave
+// tiles) of two.
+template <int D, int G, int W, bool PA, int DQ, bool PAIR>
+void launch_one(const PrefillArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((prefill_kernel<D, G, W, PA, DQ, PAIR>), dim3(a.num_items), dim3(64 * W * (PAIR ? 2 : 1)),
+                     0, s, a);
+}
+template <int D, int G, int W, int DQ, bool PAIR>
 void launch_prefill(const PrefillArgs& a, hipStream_t s) {
   if (kBlockN % a.ps_div.d == 0)
-    hipLaunchKernelGGL((prefill_kernel<D, G, W, true, DQ>), dim3(a.num_items), dim3(64 * W), 0, s, a);
+    launch_one<D, G, W, true, DQ, PAIR>(a, s);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, G, W, false, DQ>), dim3(a.num_items), dim3(64 * W), 0, s, a);
+    launch_one<D, G, W, false, DQ, PAIR>(a, s);
+}
+
+// The kernels of one shape held by this shard: launches and returns true,
+// or returns false when another shard holds them.
+template <int D, int G, int W, int DQ>
+bool launch_shape(const PrefillArgs& a, bool paired, hipStream_t s) {
+  if (paired) {
+    if constexpr (W == 4 && prefill_shard_of(D, true) == NVFP4KV_PREFILL_SHARD) {
+      launch_prefill<D, G, W, DQ, true>(a, s);
+      return true;
+    }
+    return false;
+  }
+  if constexpr (prefill_shard_of(D, false) == NVFP4KV_PREFILL_SHARD) {
+    launch_prefill<D, G, W, DQ, false>(a, s);
+    return true;
+  }
+  return false;
+}
+// The ablation and MX score modes (head_dim 128, group 4, 4-wave tiles, page
+// sizes dividing the KV tile).
+template <int DQ>
+bool launch_mode(const PrefillArgs& a, bool paired, hipStream_t s) {
+  if (paired) {
+    if constexpr (prefill_shard_of(128, true) == NVFP4KV_PREFILL_SHARD) {
+      launch_one<128, 4, 4, true, DQ, true>(a, s);
+      return true;
+    }
+    return false;
+  }
+  if constexpr (prefill_shard_of(128, false) == NVFP4KV_PREFILL_SHARD) {
+    launch_one<128, 4, 4, true, DQ, false>(a, s);
+    return true;
+  }
+  return false;
 }
 
 }  // namespace
+
+#define NVFP4KV_CAT2(x, y) x##y
+#define NVFP4KV_CAT(x, y) NVFP4KV_CAT2(x, y)
+bool NVFP4KV_CAT(launch_prefill_shard, NVFP4KV_PREFILL_SHARD)(const PrefillArgs& a, int D, int G, int W,
+                                                             int dq, bool paired, hipStream_t s) {
+  switch (dq) {
+    case 1: return launch_mode<1>(a, paired, s);
+    case 2: return launch_mode<2>(a, paired, s);
+    case 4: return launch_mode<4>(a, paired, s);
+    case 5: return launch_mode<5>(a, paired, s);
+    default: break;
+  }
+#define NVFP4KV_CASE(DD, GG, WW)                                                       \
+  if (D == DD && G == GG && W == WW)                                                   \
+    return dq == 3 ? launch_shape<DD, GG, WW, 3>(a, paired, s)                         \
+                   : dq == 0 ? launch_shape<DD, GG, WW, 0>(a, paired, s) : false;
+  NVFP4KV_CASE(128, 1, 4) NVFP4KV_CASE(128, 2, 4) NVFP4KV_CASE(128, 4, 4) NVFP4KV_CASE(128, 8, 4)
+  NVFP4KV_CASE(128, 1, 8) NVFP4KV_CASE(128, 2, 8) NVFP4KV_CASE(128, 4, 8) NVFP4KV_CASE(128, 8, 8)
+  NVFP4KV_CASE(64, 1, 4) NVFP4KV_CASE(64, 2, 4) NVFP4KV_CASE(64, 4, 4) NVFP4KV_CASE(64, 8, 4)
+#undef NVFP4KV_CASE
+  return false;
+}
+
 }  // namespace nvfp4kv
 
+#if NVFP4KV_PREFILL_SHARD == 0
 using namespace nvfp4kv;
 
 extern "C" int paged_prefill_causal(const void* q, const int32_t* qo_indptr,
@@ -1386,12 +1555,16 @@ extern "C" int paged_prefill_causal(const void* q, const int32_t* qo_indptr,
   a.B = p.batch;
   a.QT = p.q_tiles_per_head;
   if (p.schedule == kOrderStream ? !stream_order_available(p)
-                                 : p.schedule != kOrderHeaviest && p.schedule != kOrderRequest)
+      : p.schedule == kOrderPaired ? !paired_order_available(p)
+                                   : p.schedule != kOrderHeaviest && p.schedule != kOrderRequest)
     return NVFP4KV_EUNSUPPORTED;
+  const bool paired = p.schedule == kOrderPaired;
   a.order = p.schedule;
   a.nxcd = p.num_xcd > 0 ? p.num_xcd : 1;
   a.num_tiles = (uint32_t)p.num_tiles;
-  a.num_items = (uint32_t)p.num_items;
+  // paired: one workgroup per (request, KV head) and pair of Q tiles
+  a.num_items = paired ? (uint32_t)((int64_t)p.batch * p.num_kv_heads * ((p.q_tiles_per_head + 1) / 2))
+                       : (uint32_t)p.num_items;
   const int G = p.num_q_heads / p.num_kv_heads;
   const int D = p.head_dim;
   const int W = p.block_q * G / 32;  // waves per tile chosen by the plan
@@ -1419,27 +1592,11 @@ extern "C" int paged_prefill_causal(const void* q, const int32_t* qo_indptr,
                        p.num_kv_heads, p.block_q, p.q_tiles_per_head, p.split_len, p.schedule,
                        (int4*)workspace, a.counters, 2 * p.num_split_tiles);
   }
-  if (p.dequant_mode != 0 && p.dequant_mode != 3) {
-    if (p.dequant_mode == 1)
-      hipLaunchKernelGGL((prefill_kernel<128, 4, 4, true, 1>), dim3(a.num_items), dim3(256), 0, s, a);
-    else if (p.dequant_mode == 2)
-      hipLaunchKernelGGL((prefill_kernel<128, 4, 4, true, 2>), dim3(a.num_items), dim3(256), 0, s, a);
-    else if (p.dequant_mode == 4)
-      hipLaunchKernelGGL((prefill_kernel<128, 4, 4, true, 4>), dim3(a.num_items), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((prefill_kernel<128, 4, 4, true, 5>), dim3(a.num_items), dim3(256), 0, s, a);
-    return hipGetLastError() == hipSuccess ? NVFP4KV_OK : NVFP4KV_EHIP;
-  }
-#define NVFP4KV_CASE(DD, GG, WW)                                                    \
-  if (D == DD && G == GG && W == WW) {                                              \
-    if (p.dequant_mode == 3) launch_prefill<DD, GG, WW, 3>(a, s);                  \
-    else launch_prefill<DD, GG, WW, 0>(a, s);                                       \
-  } else
-  NVFP4KV_CASE(128, 1, 4) NVFP4KV_CASE(128, 2, 4) NVFP4KV_CASE(128, 4, 4) NVFP4KV_CASE(128, 8, 4)
-  NVFP4KV_CASE(128, 1, 8) NVFP4KV_CASE(128, 2, 8) NVFP4KV_CASE(128, 4, 8) NVFP4KV_CASE(128, 8, 8)
-  NVFP4KV_CASE(64, 1, 4) NVFP4KV_CASE(64, 2, 4) NVFP4KV_CASE(64, 4, 4) NVFP4KV_CASE(64, 8, 4)
-  return NVFP4KV_EUNSUPPORTED;
-#undef NVFP4KV_CASE
+  // (shape_ok and mode_ok above: exactly one shard holds the kernel)
+  const bool launched = launch_prefill_shard0(a, D, G, W, p.dequant_mode, paired, s) ||
+                        launch_prefill_shard1(a, D, G, W, p.dequant_mode, paired, s) ||
+                        launch_prefill_shard2(a, D, G, W, p.dequant_mode, paired, s);
+  if (!launched) return NVFP4KV_EUNSUPPORTED;
   return hipGetLastError() == hipSuccess ? NVFP4KV_OK : NVFP4KV_EHIP;
 }
 
@@ -1489,4 +1646,4 @@ extern "C" int paged_prefill_causal_noalloc(const void* q, const int32_t* qo_ind
   return paged_prefill_causal(q, qo_indptr, kv_indptr, page_table, kv_lens, caches, out, sm_scale,
                               plan, ws, ws ? kNoallocScratchBytes : 0, dev_error, stream);
 }
-
+#endif  // NVFP4KV_PREFILL_SHARD == 0

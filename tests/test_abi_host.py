@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol(K):
     L = ctypes.CDLL(K.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert K.lib().nvfp4kv_abi_version() == 103
+    assert K.lib().nvfp4kv_abi_version() == 104
     assert K.lib().nvfp4kv_status_string(-3).startswith(b"inconsistent")
 
 
@@ -103,9 +103,14 @@ def test_plan_max_lens(K, dtype, batch, page_size):
     assert p.head_first == int(2 * p.kv_bytes <= (32 << 20))
     assert (p.workspace_bytes == 0) == (bool(p.uniform_q) and p.split_len == 0)
     # issue order: heaviest first when the KV fits in L2, else stream order
-    # where it is available (no split; 8 KV heads; at most 8192 requests)
-    assert p.schedule == (K.SCHEDULE_HEAVIEST if p.head_first or p.split_len > 0
-                          else K.SCHEDULE_STREAM)
+    # where it is available (no split; 8 KV heads; at most 8192 requests);
+    # paired instead of heaviest first for uniform batches of 4-wave tiles
+    # that fill the 512 workgroup slots with nothing split
+    first = K.SCHEDULE_HEAVIEST if p.head_first or p.split_len > 0 else K.SCHEDULE_STREAM
+    if first == K.SCHEDULE_HEAVIEST and p.uniform_q and not wide and p.split_len == 0 \
+            and p.num_tiles >= 512:
+        first = K.SCHEDULE_PAIRED
+    assert p.schedule == first
     assert p.cu_count == 256
 
 
@@ -338,8 +343,31 @@ def test_plan_schedule_override(K):
     """A caller-chosen issue order is kept in the plan as given."""
     p = _plan(K, [0, 2048], [2048], schedule=K.SCHEDULE_REQUEST)
     assert p.schedule == K.SCHEDULE_REQUEST
-    p = _plan(K, [0, 2048], [2048])
-    assert p.schedule == K.SCHEDULE_HEAVIEST and p.head_first == 1
+    p = _plan(K, [0, 2048], [2048], schedule=K.SCHEDULE_HEAVIEST)
+    assert p.schedule == K.SCHEDULE_HEAVIEST
+
+
+def test_plan_paired_choice(K):
+    """The plan pairs light and heavy Q tiles (schedule 4) only for uniform
+    batches of 4-wave tiles that fill every workgroup slot (two per CU)
+    unsplit, with the KV in L2; otherwise it keeps its other orders."""
+    p = _plan(K, [0, 2048], [2048])  # 64 Q tiles x 8 heads = 512 = 2 x 256 CUs
+    assert (p.schedule, p.block_q, p.split_len, p.head_first) == (K.SCHEDULE_PAIRED, 32, 0, 1)
+    assert p.num_items == p.num_tiles == 512
+    p = _plan(K, [0, 2048], [2048], cu_count=304)  # 512 < 608 slots: split instead
+    assert p.split_len > 0 and p.schedule == K.SCHEDULE_HEAVIEST
+    p = _plan(K, [0, 2048], [2048], cu_count=304, split_len=-1)  # unsplit, slots not filled
+    assert p.schedule == K.SCHEDULE_HEAVIEST
+    p = _plan(K, [0, 2048, 4100], [2048, 2052])  # ragged: work list
+    assert p.schedule == K.SCHEDULE_HEAVIEST
+    p = _plan(K, [0, 2048], [2048], tile_waves=8)  # 8-wave tiles
+    assert p.schedule == K.SCHEDULE_HEAVIEST
+    p = _plan(K, [0, 2048, 4096], [2048, 2048])  # two requests, 1024 tiles
+    assert p.schedule == K.SCHEDULE_PAIRED
+    p = _plan(K, [0, 2048], [1 << 20])  # KV beyond L2: stream order
+    assert p.schedule == K.SCHEDULE_STREAM
+    p = _plan(K, [0, 4096], [4096], hq=16, hk=8, d=64)  # head_dim 64: 64 x 8 tiles
+    assert p.schedule == K.SCHEDULE_PAIRED
 
 
 def test_attention_entry_points_reject_bad_sm_scale(K):

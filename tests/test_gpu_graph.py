@@ -96,22 +96,31 @@ def test_graph_replays_match_eager(K, oracle):
         print(f"replay {r}: bit-identical to eager", flush=True)
 
 
-@pytest.mark.parametrize("mode", [3, 4, 5])
+@pytest.mark.parametrize("mode", [3, 4, 5, "paired"])
 def test_graph_prefill_other_modes(K, mode):
     """The bf16 form (mode 3) and the MX score modes (4, 5) under graph
-    capture, with split Q tiles: three replays, each after fresh queries
-    written eagerly, bit-identical to the same call made eagerly."""
+    capture, with split Q tiles, and the paired issue order on a uniform
+    batch: three replays, each after fresh queries written eagerly,
+    bit-identical to the same call made eagerly."""
     banner(f"graph capture of the prefill in dequant mode {mode}, 3 replays")
-    w = W.make_attention(f"graph_mode_{mode}", [96, 300, 1, 517], [200, 300, 700, 1100], 16, 4, 128, 16, 160,
+    paired = mode == "paired"
+    q_lens, kv_lens = ([300] * 4, [300, 500, 700, 1100]) if paired else ([96, 300, 1, 517], [200, 300, 700, 1100])
+    w = W.make_attention(f"graph_mode_{mode}", q_lens, kv_lens, 16, 4, 128, 16, 180,
                          seed=32, device="cuda", scales="amax")
     dev = "cuda"
     cache = gpu_cache(K, w)
     cache.append(w.k, w.v, w.slot_mapping)
     qo, kvp, pt, kvl = (torch.from_numpy(x).to(dev) for x in (w.qo_indptr, w.kv_indptr, w.page_table, w.kv_lens))
-    plan = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), w.num_q_heads, w.num_kv_heads,
-                  w.head_dim, w.page_size, kv_indptr=torch.from_numpy(w.kv_indptr), split_len=3, tile_waves=4,
-                  dequant_mode=mode)
-    assert plan.num_split_tiles > 0
+    if paired:
+        plan = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), w.num_q_heads,
+                      w.num_kv_heads, w.head_dim, w.page_size, kv_indptr=torch.from_numpy(w.kv_indptr),
+                      split_len=-1, tile_waves=4, schedule=K.SCHEDULE_PAIRED)
+        assert plan.workspace_bytes == 0
+    else:
+        plan = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), w.num_q_heads,
+                      w.num_kv_heads, w.head_dim, w.page_size, kv_indptr=torch.from_numpy(w.kv_indptr),
+                      split_len=3, tile_waves=4, dequant_mode=mode)
+        assert plan.num_split_tiles > 0
     q = w.q.clone()
     out = torch.empty_like(q)
     err = torch.zeros(1, dtype=torch.int32, device=dev)

@@ -121,9 +121,17 @@ def test_prefill_uniform_small_batch(K, oracle):
 
 def test_prefill_2k_full(K, oracle):
     banner("prefill 1x2048 full")
-    e, out, plan = _check(K, oracle, W.prefill_2k("cuda"))
+    w = W.prefill_2k("cuda")
+    e, out, plan = _check(K, oracle, w)
     assert plan.block_q == 32 and plan.split_len == 0  # 512 4-wave tiles fill the GPU
+    assert plan.schedule == K.SCHEDULE_PAIRED
     print(f"max err {e:.3g}")
+    # heaviest first (one 4-wave tile per workgroup): the same bits
+    heavy = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), 32, 8, 128, 16,
+                   kv_indptr=torch.from_numpy(w.kv_indptr), schedule=K.SCHEDULE_HEAVIEST)
+    o2, _, _ = run_gpu(K, w, plan=heavy)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, out)
 
 
 def test_prefill_uniform_1k_sampled(K, oracle):
@@ -353,3 +361,70 @@ def test_prefill_dequant_ablation_unsupported_shape(K, mode):
                        tile_waves=4, dequant_mode=mode)
         with pytest.raises(K.NVFP4KVError, match="unsupported"):
             run_gpu(K, w2, plan=plan2)
+
+
+# Paired issue order: uniform batches whose Q tiles t and QT - 1 - t share one
+# 8-wave workgroup (the light tile's waves stage every KV tile).  Shapes: both
+# head dims, every GQA group, an odd Q tile count (the middle tile alone), a
+# single Q tile (no light tile), page sizes dividing the KV tile and not,
+# the bf16 form, and the ablation and MX score modes.
+PAIRED_CASES = [
+    ("g4_d128", [256] * 3, [300] * 3, 32, 8, 128, 16, 0),
+    ("g4_d128_odd_tiles", [160] * 2, [400] * 2, 32, 8, 128, 16, 0),
+    ("g4_d128_one_tile", [20] * 3, [90] * 3, 32, 8, 128, 16, 0),
+    ("g1_d128_ps5", [200] * 2, [333] * 2, 8, 8, 128, 5, 0),
+    ("g2_d128_bf16", [100] * 3, [100, 300, 700], 16, 8, 128, 16, 3),
+    ("g8_d128_ps32", [64] * 2, [64, 1000], 64, 8, 128, 32, 0),
+    ("g4_d64", [300] * 2, [300, 450], 16, 4, 64, 16, 0),
+    ("g8_d64_ps48_bf16", [77] * 3, [77, 500, 1200], 16, 2, 64, 48, 3),
+    ("g4_d128_mode1", [200] * 2, [260] * 2, 32, 8, 128, 16, 1),
+    ("g4_d128_mode2", [200] * 2, [260] * 2, 32, 8, 128, 16, 2),
+    ("g4_d128_mode4", [200] * 2, [260] * 2, 32, 8, 128, 16, 4),
+    ("g4_d128_mode5", [200] * 2, [260] * 2, 32, 8, 128, 16, 5),
+]
+
+
+@pytest.mark.parametrize("case", PAIRED_CASES, ids=[c[0] for c in PAIRED_CASES])
+def test_paired_order(K, oracle, case):
+    """Paired issue computes every row as heaviest-first issue does: bitwise
+    the same outputs; and (modes 0-3) the oracle parity."""
+    name, q, kv, hq, hk, d, ps, mode = case
+    banner(f"paired order {name}")
+    pool = sum((k + ps - 1) // ps for k in kv) + 5
+    w = W.make_attention(f"paired_{name}", q, kv, hq, hk, d, ps, pool, seed=33, device="cuda",
+                         scales="amax")
+
+    def mk(schedule):
+        return K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), hq, hk, d, ps,
+                      kv_indptr=torch.from_numpy(w.kv_indptr), split_len=-1, tile_waves=4,
+                      dequant_mode=mode, schedule=schedule)
+
+    base, cache, _ = run_gpu(K, w, plan=mk(K.SCHEDULE_HEAVIEST))
+    out, _, plan = run_gpu(K, w, cache=cache, plan=mk(K.SCHEDULE_PAIRED))
+    torch.cuda.synchronize()
+    assert K.read_device_error("cuda") == 0
+    assert torch.equal(out, base)
+    print(f"Q tiles per head {plan.q_tiles_per_head}: bitwise equal to heaviest first")
+    if mode <= 3:
+        ref, rows = oracle_outputs(oracle, w)
+        e = assert_close(out.index_select(0, torch.from_numpy(rows).cuda()), ref, w.name)
+        print(f"max err {e:.3g}")
+
+
+def test_paired_order_unavailable(K):
+    """Paired issue needs a uniform batch (no work list), 4-wave tiles and no
+    split: other requests are refused before any launch."""
+    banner("paired order where it is not available")
+    w = W.make_attention("paired_no", [64, 100], [64, 100], 32, 8, 128, 16, 20, seed=34, device="cuda")
+    u = W.make_attention("paired_no_u", [128] * 2, [128] * 2, 32, 8, 128, 16, 20, seed=34, device="cuda")
+
+    def mk(x, **kw):
+        return K.plan(torch.from_numpy(x.qo_indptr), torch.from_numpy(x.kv_lens), 32, 8, 128, 16,
+                      kv_indptr=torch.from_numpy(x.kv_indptr), schedule=K.SCHEDULE_PAIRED, **kw)
+
+    for x, kw in ((w, dict(split_len=-1)), (u, dict(split_len=1)), (u, dict(split_len=-1, tile_waves=8))):
+        with pytest.raises(K.NVFP4KVError, match="unsupported"):
+            run_gpu(K, x, plan=mk(x, **kw))
+    out, _, plan = run_gpu(K, u, plan=mk(u, split_len=-1, tile_waves=4))
+    torch.cuda.synchronize()
+    assert plan.schedule == K.SCHEDULE_PAIRED and K.read_device_error("cuda") == 0
