@@ -20,7 +20,8 @@ divided by the step time).  Also reported:
     fractions of the MI355X roofline, and the prefill kernel on equal-cost
     tiles (64 x 32 queries over 8192 keys: no causal imbalance);
   * schedule: the prefill of the two large batches under the three issue
-    orders (heaviest first, stream order, request order);
+    orders (heaviest first, stream order, request order), and of the
+    2048x2048 batch heaviest first and paired (the plan's choice);
   * the decode step, the dequant-placement ablation, the measured achievable
     peaks, the plan's host time, and the CPU oracle timed on bounded samples.
 
@@ -196,7 +197,8 @@ def main():
     G = w.num_q_heads // w.num_kv_heads
     paired = plan.schedule == K.SCHEDULE_PAIRED
     kernel_name = (f"prefill_kernel<{w.head_dim},{G},{plan.block_q * G // 32},"
-                   f"{'true' if 64 % w.page_size == 0 else 'false'},0,{'true' if paired else 'false'}>")
+                   f"{'true' if 64 % w.page_size == 0 else 'false'},{plan.dequant_mode},"
+                   f"{'true' if paired else 'false'}>")
     traffic = _traffic("prefill_2k")
     frac = pre_tflops / BF16_PEAK_TFLOPS
     result = {
@@ -211,13 +213,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": 1, "q_len": 2048, "kv_len": 2048,
                    "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128, "page_size": 16,
                    "kv_format": "nvfp4 (e2m1 + e4m3 per 16, fp32 global scale)",
-                   "staging": "f16 LDS tile, f16 MFMA (the bf16 form, bf16 staging + bf16 MFMA, is "
-                              "dequant_mode 3: configs.*.prefill_bf16)",
+                   "staging": "bf16 LDS tile, bf16 MFMA (dequant_mode 3; the f16 form, f16 staging + f16 "
+                              "MFMA, is dequant_mode 0: configs.*.prefill_f16)",
                    "step": "append 2048 K/V rows + causal paged prefill",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": kernel_name, "schedule": SCHEDULE_NAMES[plan.schedule],
@@ -278,8 +280,8 @@ def main():
         c2.append(w2.k, w2.v, w2.slot_mapping)
         result["dequant_ablation"] = bench_dequant_ablation(K, w2, c2, (qo_d, kvp_d, pt_d, kvl_d),
                                                             torch.empty_like(w2.q), torch)
-        # the bf16 form on this batch (4-wave tiles, as the plan picks for it)
-        configs["prefill_2k"]["prefill_bf16"] = result["dequant_ablation"]["lds_once_per_tile_bf16"]
+        # the f16 form on this batch (paired 4-wave tiles, as the plan picks for it)
+        configs["prefill_2k"]["prefill_f16"] = result["dequant_ablation"]["lds_once_per_tile"]
         del w2, c2
     if not args.no_achievable:
         ach = bench_achievable(K, W, dev, torch, np)
@@ -338,14 +340,14 @@ def bench_config_small(K, W, dev, torch):
                   w.num_kv_heads, w.head_dim, w.page_size)
     out = torch.empty_like(w.q)
     pre = graph_launch_ms(torch, lambda: K.paged_prefill_causal(w.q, *args, cache, out, w.sm_scale, plan=plan))
-    plan3 = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), w.num_q_heads,
-                   w.num_kv_heads, w.head_dim, w.page_size, dequant_mode=3)
-    pre3 = graph_launch_ms(torch, lambda: K.paged_prefill_causal(w.q, *args, cache, out, w.sm_scale, plan=plan3))
+    plan0 = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), w.num_q_heads,
+                   w.num_kv_heads, w.head_dim, w.page_size, dequant_mode=0)
+    pre0 = graph_launch_ms(torch, lambda: K.paged_prefill_causal(w.q, *args, cache, out, w.sm_scale, plan=plan0))
     app = graph_launch_ms(torch, lambda: cache.append(w.k, w.v, w.slot_mapping))
     flops = attention_flops(w.q_lens, w.kv_lens, w.num_q_heads, w.head_dim)
     nbytes = append_bytes(int(w.kv_lens.sum()), w.num_kv_heads, w.head_dim)
     return {"workload": w.name, "prefill": {"flops_per_launch": flops, **tflops_row(flops, pre)},
-            "prefill_bf16": {"dequant_mode": 3, **tflops_row(flops, pre3)},
+            "prefill_f16": {"dequant_mode": 0, **tflops_row(flops, pre0)},
             "append": {"bytes_per_launch": nbytes, **gbs_row(nbytes, app)},
             "note": "a few microseconds of work: bound by launch latency, not by the roofline"}
 
@@ -406,14 +408,14 @@ def bench_config_large(K, w, torch, chunk_append=False):
     plan = mk()
     pre = graph_launch_ms(torch, lambda: K.paged_prefill_causal(w.q, *args, cache, out, w.sm_scale, plan=plan),
                           per_graph=4, replays=3)
-    plan3 = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), w.num_q_heads,
-                   w.num_kv_heads, w.head_dim, w.page_size, dequant_mode=3)
-    pre3 = graph_launch_ms(torch, lambda: K.paged_prefill_causal(w.q, *args, cache, out, w.sm_scale, plan=plan3),
+    plan0 = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), w.num_q_heads,
+                   w.num_kv_heads, w.head_dim, w.page_size, dequant_mode=0)
+    pre0 = graph_launch_ms(torch, lambda: K.paged_prefill_causal(w.q, *args, cache, out, w.sm_scale, plan=plan0),
                            per_graph=4, replays=3)
     row = {"workload": w.name, "prefill": {"flops_per_launch": flops, "schedule": plan.schedule,
                                            "block_q": plan.block_q, "split_len": plan.split_len,
                                            **tflops_row(flops, pre)},
-           "prefill_bf16": {"dequant_mode": 3, **tflops_row(flops, pre3)},
+           "prefill_f16": {"dequant_mode": 0, **tflops_row(flops, pre0)},
            "append": {"bytes_per_launch": nbytes, "rows": int(k.shape[0]), **gbs_row(nbytes, app)}}
     sched = {}
     for name, s in (("heaviest_first", K.SCHEDULE_HEAVIEST), ("stream_order", K.SCHEDULE_STREAM),
@@ -434,12 +436,13 @@ def bench_config_large(K, w, torch, chunk_append=False):
 
 def bench_dequant_ablation(K, w, cache, dev_args, out, torch, per_graph=50, replays=20):
     """The 2048x2048 prefill under the dequant placements of the PR #4769
-    page's comparison (graph-timed launches; 4-wave tiles, as the plan picks):
-    tiles decoded once per workgroup into f16 LDS (the kernel's own design), K
-    decoded in registers inside the matrix loop, a byte-table decode, the
-    f16 design with bf16 staging and bf16 matrix instructions instead, and
-    the native low-precision scores (K requantized to MXFP4, or MXFP8,
-    while staged, Q in MXFP8, the scaled matrix instruction; looser accuracy
+    page's comparison (graph-timed launches; paired 4-wave tiles, as the plan
+    picks): tiles decoded once per workgroup into f16 LDS, K decoded in
+    registers inside the matrix loop, a byte-table decode (the three in f16,
+    bitwise the same outputs), tiles decoded once into bf16 LDS with bf16
+    matrix instructions (the kernel's own design, the plan's choice), and the
+    native low-precision scores (K requantized to MXFP4, or MXFP8, while
+    staged, Q in MXFP8, the scaled matrix instruction; looser accuracy
     contracts of their own)."""
     flops = attention_flops(w.q_lens, w.kv_lens, w.num_q_heads, w.head_dim)
     res = {}

@@ -136,17 +136,22 @@ typedef struct {
                                workgroup each; under schedule 4 two Q tiles
                                share one workgroup) */
   int64_t num_split_tiles;  /* Q tiles (x KV heads) whose KV range is split */
-  /* Dequant-placement ablation (the PR #4769 page's before/after comparison);
-     the plan sets 0 and a caller may change it before paged_prefill_causal:
-       0  each NVFP4 KV tile decoded once per workgroup into an f16 LDS tile
-          (hardware FP4 conversion) -- the kernel's own design;
-       1  K codes and scales staged raw in LDS, every wave decoding its K
-          operand fragments in registers inside the matrix loop (V as 0);
+  /* Staging form and dequant-placement ablation (the PR #4769 page's
+     before/after comparison); the plan sets 3 and a caller may change it
+     before paged_prefill_causal:
+       3  each NVFP4 KV tile decoded once per workgroup into a bf16 LDS tile
+          (every E2M1 x E4M3 product is exact in bf16), bf16 queries and
+          probabilities, bf16 matrix instructions -- the kernel's own design
+          and the plan's choice; every kernel shape;
+       0  the same with an f16 staging tile (exact as well), f16 queries
+          after an exact power-of-two rescale per row and f16 probabilities
+          (three more significant bits), f16 matrix instructions; every
+          kernel shape (the f16 form the ablation modes 1 and 2 vary);
+       1  as 0 with K codes and scales staged raw in LDS, every wave
+          decoding its K operand fragments in registers inside the matrix
+          loop (V as 0);
        2  as 0, decoding the codes with a byte table (v_perm) instead of the
           hardware conversion;
-       3  as 0 with a bf16 staging tile, bf16 queries and probabilities and
-          bf16 matrix instructions (0 stages f16: exact as well, fewer
-          instructions); every shape mode 0 has;
        4  native low-precision scores ([PR #4769] code analysis: the branch
           for matrix cores that take E2M1 operands): K requantized while
           staged from NVFP4 (E4M3 scale per 16) to MXFP4 (E8M0 scale per
@@ -234,11 +239,11 @@ int nvfp4_prefill_plan(const int32_t* qo_indptr_host, const int32_t* kv_lens_hos
 /*
  * paged_prefill_causal -- batched causal prefill attention over the NVFP4
  * paged cache ([PR #4769]: each KV tile is dequantized once into a 16-bit LDS
- * staging tile outside the matrix-core loop -- f16 by default, since every
- * E2M1 x E4M3 product is exact in f16 and the queries enter the f16 matrix
- * instructions after an exact power-of-two rescale per row; bf16 staging
- * with bf16 matrix instructions is plan->dequant_mode 3; [PR #3575]: O(1)
- * tile decode for uniform batches, heaviest-first Q tiles, L2-gated order).
+ * staging tile outside the matrix-core loop -- bf16 by default (plan->
+ * dequant_mode 3), since every E2M1 x E4M3 product is exact in bf16, with
+ * bf16 queries and probabilities on bf16 matrix instructions; the f16 form
+ * is dequant_mode 0; [PR #3575]: O(1) tile decode for uniform batches,
+ * heaviest-first Q tiles, L2-gated order).
  *   q          bf16 [total_q][num_q_heads][head_dim], contiguous, 16-byte aligned.
  *   qo_indptr  int32 [batch+1] (device copy of the plan's host array).
  *   kv_indptr  int32 [batch+1]: request r's pages are

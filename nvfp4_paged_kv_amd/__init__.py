@@ -280,7 +280,7 @@ class Plan:
 
     def __init__(self, qo_indptr, kv_lens, num_q_heads, num_kv_heads, head_dim, page_size,
                  kv_indptr=None, l2_bytes: int = 0, split_len: int = 0, tile_waves: int = 0,
-                 dequant_mode: int = 0, cu_count: int = 0, schedule: int = 0):
+                 dequant_mode: Optional[int] = None, cu_count: int = 0, schedule: int = 0):
         qo = _host_int32(qo_indptr, "qo_indptr")
         kvl = _host_int32(kv_lens, "kv_lens")
         kvp = _host_int32(kv_indptr, "kv_indptr") if kv_indptr is not None else None
@@ -291,7 +291,8 @@ class Plan:
             _ptr(qo), _ptr(kvl), _ptr(kvp), kvl.numel(), num_q_heads, num_kv_heads, head_dim,
             page_size, l2_bytes, cu_count, split_len, tile_waves, ctypes.byref(self.struct)),
             "nvfp4_prefill_plan")
-        self.struct.dequant_mode = int(dequant_mode)
+        if dequant_mode is not None:
+            self.struct.dequant_mode = int(dequant_mode)
         if schedule:
             self.struct.schedule = int(schedule)
         self.qo_host, self.kv_lens_host, self.kv_indptr_host = qo, kvl, kvp
@@ -336,17 +337,18 @@ SCHEDULE_HEAVIEST, SCHEDULE_STREAM, SCHEDULE_REQUEST, SCHEDULE_PAIRED = 1, 2, 3,
 
 
 def plan(qo_indptr, kv_lens, num_q_heads, num_kv_heads, head_dim, page_size, kv_indptr=None,
-         l2_bytes: int = 0, split_len: int = 0, tile_waves: int = 0, dequant_mode: int = 0,
+         l2_bytes: int = 0, split_len: int = 0, tile_waves: int = 0, dequant_mode: Optional[int] = None,
          cu_count: int = 0, schedule: int = 0) -> Plan:
     """Host plan of one prefill batch.  l2_bytes / cu_count: device L2 and CU
     count to plan for (0: the current device's); split_len: KV tiles per chunk
     of a split Q tile (0 automatic, > 0 forced, < 0 never); tile_waves: waves
     of 32 query rows per workgroup (0 automatic, 4 or 8); dequant_mode: the
-    dequant-placement ablation (0: tiles decoded once into f16 LDS, the
-    default; 1: K decoded in registers inside the matrix loop; 2: byte-table
-    decode; 3: bf16 staging and bf16 matrix instructions, for every shape; 4 and 5: native
-    MX scores -- MXFP4 (4) or MXFP8 (5) keys, MXFP8 queries, the scaled
-    matrix instruction, under looser accuracy contracts); schedule: issue
+    staging form and dequant-placement ablation (None: the plan's choice, 3;
+    3: tiles decoded once into a bf16 LDS tile, bf16 queries, probabilities
+    and matrix instructions; 0: the same in f16; 1: as 0 with K decoded in
+    registers inside the matrix loop; 2: as 0 with a byte-table decode; 4
+    and 5: native MX scores -- MXFP4 (4) or MXFP8 (5) keys, MXFP8 queries,
+    the scaled matrix instruction, under looser accuracy contracts); schedule: issue
     order of the Q tiles (0: the plan's choice; SCHEDULE_HEAVIEST,
     SCHEDULE_STREAM, SCHEDULE_REQUEST, or SCHEDULE_PAIRED -- Q tiles t and
     QT - 1 - t of a uniform, unsplit batch of 4-wave tiles in one 8-wave

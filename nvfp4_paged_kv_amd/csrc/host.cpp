@@ -68,6 +68,9 @@ extern "C" int nvfp4_prefill_plan(const int32_t* qo_indptr_host, const int32_t* 
   // of the current device)
   const int cus = cu_count > 0 ? cu_count : device_props().cu_count;
   p.cu_count = cus;
+  // bf16 staging tile, bf16 queries and probabilities, bf16 matrix
+  // instructions (dequant mode 3)
+  p.dequant_mode = 3;
   p.block_n = kBlockN;
   // One pass of reductions over the host arrays ([PR #5043]: max lengths from
   // a vectorised reduction, not a per-request Python loop).
@@ -253,4 +256,4 @@ extern "C" const char* nvfp4kv_status_string(int status) {
   }
 }
 
-extern "C" int nvfp4kv_abi_version(void) { return 104; }
+extern "C" int nvfp4kv_abi_version(void) { return 105; }

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol(K):
     L = ctypes.CDLL(K.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert K.lib().nvfp4kv_abi_version() == 104
+    assert K.lib().nvfp4kv_abi_version() == 105
     assert K.lib().nvfp4kv_status_string(-3).startswith(b"inconsistent")
 
 
@@ -353,6 +353,8 @@ def test_plan_paired_choice(K):
     unsplit, with the KV in L2; otherwise it keeps its other orders."""
     p = _plan(K, [0, 2048], [2048])  # 64 Q tiles x 8 heads = 512 = 2 x 256 CUs
     assert (p.schedule, p.block_q, p.split_len, p.head_first) == (K.SCHEDULE_PAIRED, 32, 0, 1)
+    assert p.dequant_mode == 3  # bf16 staging, bf16 matrix instructions
+    assert _plan(K, [0, 2048], [2048], dequant_mode=0).dequant_mode == 0
     assert p.num_items == p.num_tiles == 512
     p = _plan(K, [0, 2048], [2048], cu_count=304)  # 512 < 608 slots: split instead
     assert p.split_len > 0 and p.schedule == K.SCHEDULE_HEAVIEST

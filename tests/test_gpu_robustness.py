@@ -5,12 +5,13 @@ plain definition:
   repeated runs give the same bits whichever chunk finishes last, and every
   call zeroes its arrival counters itself, so stale counters left in the
   workspace (by an earlier call, or its first contents) change nothing;
-* query rows far from N(0, 1): the kernels feed the f16 matrix instructions
-  with each bf16 query row rescaled by a power of two (its largest magnitude
-  to [2^14, 2^15)), so rows with a huge magnitude, rows of bf16 subnormals
-  and rows whose elements span more than 2^30 are compared with the fp64
-  oracle at the usual tolerance, in the prefill (both tile widths) and the
-  decode;
+* query rows far from N(0, 1): the kernels rescale each bf16 query row by a
+  power of two (its largest magnitude to [2^14, 2^15)) before the 16-bit
+  matrix instructions (bf16 in the prefill's default form, f16 in its mode 0
+  and in the decode), so rows with a huge magnitude, rows of bf16
+  subnormals and rows whose elements span more than 2^30 are compared with
+  the fp64 oracle at the usual tolerance, in the prefill (both tile widths;
+  the f16 form in test_gpu_f16_staging.py) and the decode;
 * a global k/v scale that is not positive finite: the prefill and the decode
   set NVFP4KV_DEV_BAD_SCALE_ATTN and every kernel runs to its end (the next
   call with good scales is exact again).
