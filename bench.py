@@ -103,6 +103,9 @@ def main():
                     help="only run a plain 256 MiB device copy (HBM-counter calibration)")
     ap.add_argument("--steady-only", action="store_true",
                     help="only launch the 2048x2048 prefill and the steady-state batch (for counters)")
+    ap.add_argument("--steady-dequant-mode", type=int, default=None,
+                    help="with --steady-only: the staging form of both prefills (default: the plan's, "
+                         "3 = bf16; 0 = f16)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -139,11 +142,13 @@ def main():
 
     if args.steady_only:
         cache.append(w.k, w.v, w.slot_mapping)
-        plan = K.plan(qo_h, kvl_h, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size, kv_indptr=kvp_h)
+        plan = K.plan(qo_h, kvl_h, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size, kv_indptr=kvp_h,
+                      dequant_mode=args.steady_dequant_mode)
         for _ in range(60):
             K.paged_prefill_causal(w.q, qo_d, kvp_d, pt_d, kvl_d, cache, out, w.sm_scale, plan=plan)
         torch.cuda.synchronize()
-        print(json.dumps({"steady_state": bench_steady(K, W, dev, torch, launches=12)}), flush=True)
+        print(json.dumps({"steady_state": bench_steady(K, W, dev, torch, launches=12,
+                                                       dequant_mode=args.steady_dequant_mode)}), flush=True)
         return
     if args.ablation_only:
         cache.append(w.k, w.v, w.slot_mapping)
@@ -352,7 +357,7 @@ def bench_config_small(K, W, dev, torch):
             "note": "a few microseconds of work: bound by launch latency, not by the roofline"}
 
 
-def bench_steady(K, W, dev, torch, launches=0):
+def bench_steady(K, W, dev, torch, launches=0, dequant_mode=None):
     """The prefill kernel of the 2048x2048 batch (4-wave tiles, no KV split)
     on equal-cost tiles: 64 requests x 32 queries over 8192 keys, 512 tiles
     of 128 KV tiles each, two per CU, so neither causal imbalance nor the
@@ -364,7 +369,8 @@ def bench_steady(K, W, dev, torch, launches=0):
     args = _dev_arrays(w, dev, torch)
     out = torch.empty_like(w.q)
     plan = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), w.num_q_heads, w.num_kv_heads,
-                  w.head_dim, w.page_size, kv_indptr=torch.from_numpy(w.kv_indptr), tile_waves=4, split_len=-1)
+                  w.head_dim, w.page_size, kv_indptr=torch.from_numpy(w.kv_indptr), tile_waves=4, split_len=-1,
+                  dequant_mode=dequant_mode)
     fn = lambda: K.paged_prefill_causal(w.q, *args, cache, out, w.sm_scale, plan=plan)
     flops = attention_flops(w.q_lens, w.kv_lens, w.num_q_heads, w.head_dim)
     if launches:
