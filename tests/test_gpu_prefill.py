@@ -186,6 +186,39 @@ def test_prefill_random_shapes(K, oracle, seed):
     print(f"max err {e:.3g}; tiles {plan.num_tiles}, split {plan.split_len}, chunks {plan.max_chunks}")
 
 
+@pytest.mark.parametrize("mode,split,waves", [(3, -1, 4), (3, 2, 4), (0, 0, 8), (3, -1, 8)])
+def test_prefill_empty_requests(K, oracle, mode, split, waves):
+    """Requests without queries, with and without cached keys, between
+    ordinary ones (a non-uniform batch: the device work list), with no,
+    forced and automatic KV splits, both staging forms and both tile widths:
+    the empty requests own no output rows and every other row matches the
+    oracle."""
+    q = [0, 37, 0, 100, 0, 1, 0]
+    kv = [0, 200, 50, 100, 0, 64, 0]
+    banner(f"prefill empty requests mode={mode} split={split} waves={waves}")
+    w = W.make_attention(f"prefill_empty_{mode}_{split}_{waves}", q, kv, 32, 8, 128, 16, 40, seed=51,
+                         device="cuda", scales="amax")
+    plan = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), w.num_q_heads, w.num_kv_heads,
+                  w.head_dim, w.page_size, kv_indptr=torch.from_numpy(w.kv_indptr), split_len=split,
+                  tile_waves=waves, dequant_mode=mode)
+    assert plan.uniform_q == 0 and plan.total_q == sum(q)
+    e, _, plan = _check(K, oracle, w, plan=plan)
+    print(f"max err {e:.3g}; split {plan.split_len}")
+
+
+def test_prefill_without_queries_launches_nothing(K):
+    """A batch with no query rows -- every request empty (one of them with
+    cached keys), or no request at all -- plans no tile, launches nothing and
+    leaves the device error word clear."""
+    for q, kv in (([0, 0, 0], [0, 30, 0]), ([], [])):
+        banner(f"prefill without queries q={q} kv={kv}")
+        w = W.make_attention("prefill_noq", q, kv, 8, 2, 64, 16, 4, seed=52, device="cuda")
+        out, _, plan = run_gpu(K, w)
+        torch.cuda.synchronize()
+        assert plan.num_tiles == 0 and out.numel() == 0
+        assert K.read_device_error("cuda") == 0
+
+
 def test_schedule_orders_give_identical_bits(K):
     """Uniform O(1) decode and the device work list, each in the three issue
     orders (heaviest first, stream order, request order), and split Q tiles

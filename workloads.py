@@ -38,7 +38,7 @@ def normal_bf16(shape, seed, stream, device, std=1.0, chunk_rows=1 << 16) -> tor
     """bf16 tensor ~ std * N(0,1), drawn in fp32 and rounded to nearest-even."""
     g = _gen(seed, stream, device)
     out = torch.empty(shape, dtype=torch.bfloat16, device=device)
-    flat = out.view(shape[0], -1)
+    flat = out.view(shape[0], math.prod(shape[1:]))  # (also for zero rows)
     for r0 in range(0, shape[0], chunk_rows):
         r1 = min(shape[0], r0 + chunk_rows)
         x = torch.randn((r1 - r0, flat.shape[1]), generator=g, device=device, dtype=torch.float32)
@@ -52,7 +52,7 @@ def student_t3_bf16(shape, seed, stream, device, chunk_rows=1 << 14) -> torch.Te
     """bf16 tensor ~ Student-t with 3 degrees of freedom: Z / sqrt(chi2_3 / 3)."""
     g = _gen(seed, stream, device)
     out = torch.empty(shape, dtype=torch.bfloat16, device=device)
-    flat = out.view(shape[0], -1)
+    flat = out.view(shape[0], math.prod(shape[1:]))  # (also for zero rows)
     for r0 in range(0, shape[0], chunk_rows):
         r1 = min(shape[0], r0 + chunk_rows)
         n = (r1 - r0, flat.shape[1])
