@@ -106,6 +106,9 @@ def main():
     ap.add_argument("--steady-dequant-mode", type=int, default=None,
                     help="with --steady-only: the staging form of both prefills (default: the plan's, "
                          "3 = bf16; 0 = f16)")
+    ap.add_argument("--power", action="store_true",
+                    help="only sample board power and shader clocks (amd-smi) while the 2048x2048 "
+                         "prefill and the MFMA-only loop with random operands run back to back")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -130,6 +133,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": src.numel(), "launches": 5}))
+        return
+    if args.power:
+        print(json.dumps(power_telemetry(K, W, dev, torch, np)))
         return
     w = W.prefill_2k(dev)
     cache = K.PagedCache.empty(w.num_pages, w.page_size, w.num_kv_heads, w.head_dim, dev,
@@ -679,6 +685,83 @@ def bench_achievable(K, W, dev, torch, np):
     out["mfma_bf16_random_operands_TFLOPs"] = round(
         L.nvfp4kv_mfma_peak_probe_flops(blocks, iters) / timed(mfma_random) / 1e12, 1)
     return out
+
+
+def power_telemetry(K, W, dev, torch, np, secs=6.0, period=0.3):
+    """Board power and shader clocks while the 2048x2048 prefill (the plan's
+    kernel, back to back) and then the MFMA-only loop of peak.hip with random
+    operand bits run for `secs` seconds each: `amd-smi metric -p -c` sampled
+    every `period` seconds from a thread; per phase the median socket power
+    and the median over samples of the lowest and highest of the reported
+    gfx clocks, the first second of each phase dropped (the readings lag)."""
+    import ctypes
+    import re
+    import subprocess
+    import threading
+    from nvfp4_paged_kv_amd.build import PEAK_LIB
+    samples, phase, done = [], ["idle"], threading.Event()
+
+    def poll():
+        while not done.is_set():
+            t = time.time()
+            r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True,
+                               timeout=10)
+            p = re.search(r'"socket_power":\s*\{\s*"value":\s*(\d+)', r.stdout)
+            clk = [int(x) for x in re.findall(r'"gfx_\d+":\s*\{\s*"clk":\s*\{\s*"value":\s*(\d+)', r.stdout)]
+            if p and clk:
+                samples.append((phase[0], t, int(p.group(1)), min(clk), max(clk)))
+            done.wait(period)
+
+    w = W.prefill_2k(dev)
+    cache = K.PagedCache.empty(w.num_pages, w.page_size, w.num_kv_heads, w.head_dim, dev, w.k_scale, w.v_scale)
+    cache.append(w.k, w.v, w.slot_mapping)
+    args = _dev_arrays(w, dev, torch)
+    out = torch.empty_like(w.q)
+    plan = K.plan(torch.from_numpy(w.qo_indptr), torch.from_numpy(w.kv_lens), w.num_q_heads, w.num_kv_heads,
+                  w.head_dim, w.page_size)
+    L = ctypes.CDLL(PEAK_LIB)
+    L.nvfp4kv_mfma_random_peak_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    blocks, iters = 256 * 4, 2000
+    buf = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+
+    def mfma():
+        if L.nvfp4kv_mfma_random_peak_probe(blocks, iters, ctypes.c_void_p(buf.data_ptr()), stream) != 0:
+            raise SystemExit("MFMA peak probe launch failed")
+
+    flops = attention_flops(w.q_lens, w.kv_lens, w.num_q_heads, w.head_dim)
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    time.sleep(1.5)
+    res = {"sampler": "amd-smi metric -p -c --json", "period_s": period}
+    for name, fn in (("prefill_2048x2048", lambda: K.paged_prefill_causal(w.q, *args, cache, out, w.sm_scale,
+                                                                            plan=plan)),
+                     ("mfma_loop_random_operands", mfma)):
+        phase[0] = name
+        t0, n = time.time(), 0
+        while time.time() - t0 < secs:
+            for _ in range(20):
+                fn()
+            torch.cuda.synchronize()
+            n += 20
+        res[name] = {"launches": n, "avg_launch_us": round((time.time() - t0) / n * 1e6, 2), "t0": t0}
+        phase[0] = "idle"
+        time.sleep(1.5)
+    done.set()
+    th.join()
+    res["prefill_2048x2048"]["TFLOP_s"] = round(flops / (res["prefill_2048x2048"]["avg_launch_us"] * 1e-6) / 1e12, 1)
+    for name in ("prefill_2048x2048", "mfma_loop_random_operands"):
+        r = res[name]
+        t_start = r.pop("t0")
+        sel = [s for s in samples if s[0] == name and s[1] > t_start + 1.0]
+        r["samples"] = len(sel)
+        if sel:
+            r["socket_power_W"] = float(np.median([s[2] for s in sel]))
+            r["gfx_clk_MHz_low"] = float(np.median([s[3] for s in sel]))
+            r["gfx_clk_MHz_high"] = float(np.median([s[4] for s in sel]))
+    idle = [s[2] for s in samples if s[0] == "idle"]
+    res["idle_socket_power_W"] = float(np.min(idle)) if idle else None
+    return res
 
 
 def bench_append_stress(K, W, dev, torch, np, iters=12, sets=4, rounds=3, replays=2):
