@@ -236,17 +236,21 @@ __device__ __forceinline__ f32x16 mma16(f16x8 a, f16x8 b, f32x16 c) {
 __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
   return __builtin_amdgcn_perm(f2u(hi), f2u(lo), 0x07060302u);
 }
+// 8 codes (one dword) times their block scale S as bf16 pairs: each code
+// pair to f32, one f32 multiply per element (exact), the upper halves kept.
+__device__ __forceinline__ u32x4 decode8_bf16(uint32_t x, float S) {
+  u32x4 r;
+  static_for<0, 4>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    const f32x2 f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, j);
+    r[j] = bf16_pair(f[0] * S, f[1] * S);
+  });
+  return r;
+}
 template <int DQ>
 __device__ __forceinline__ u32x4 decode8(uint32_t x, f16x2 SS) {
   if constexpr (DQ == 3) {
-    const float S = (float)SS[0];
-    u32x4 r;
-    static_for<0, 4>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      const f32x2 f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(x, 1.0f, j);
-      r[j] = bf16_pair(f[0] * S, f[1] * S);
-    });
-    return r;
+    return decode8_bf16(x, (float)SS[0]);
   } else if constexpr (DQ != 2) {
     return (u32x4){fp4x2_times<0>(x, SS), fp4x2_times<1>(x, SS), fp4x2_times<2>(x, SS),
                    fp4x2_times<3>(x, SS)};
@@ -518,6 +522,7 @@ struct TileStager {
   static constexpr int PIECES = 8 * C::JOBS_PER_THREAD;
   uint8_t* rowp[C::JOBS_PER_THREAD];
   uint32_t S01[C::JOBS_PER_THREAD];  // the part's two E4M3 scales as an f16 pair (exact)
+  f32x2 S32[C::JOBS_PER_THREAD];     // (DQ 3) the same two scales in f32, as the bf16 decode uses them
   uint32_t sw[C::JOBS_PER_THREAD];   // the part's two raw scale bytes
   uint8_t* sfp;                      // (DQ 1) where the K part's scale bytes go
   u32x4 chunk;
@@ -540,8 +545,11 @@ struct TileStager {
       // both E4M3 scales of the part in one conversion (dead keys: zero scales)
       sw[j] = live ? (scale_word<D>(job[j], part) >> (16 * (part & 1))) & 0xFFFFu : 0u;
       const f32x2 S = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw[j], 1.0f, false);
-      const f16x2 Sh = {(_Float16)S[0], (_Float16)S[1]};
-      S01[j] = __builtin_bit_cast(uint32_t, Sh);
+      S32[j] = S;
+      if constexpr (DQ != 3) {
+        const f16x2 Sh = {(_Float16)S[0], (_Float16)S[1]};
+        S01[j] = __builtin_bit_cast(uint32_t, Sh);
+      }
       if constexpr (DQ >= 4) {
         if (j == 0) {
           // The part's blocks 2p + k (k = 0, 1) pair with blocks 2(p^1) + k
@@ -613,11 +621,14 @@ struct TileStager {
         *(u32x4*)rowp[0] = job[0].pk;
         *(uint16_t*)sfp = (uint16_t)sw[0];
       }
+    } else if constexpr (DQ == 3) {
+      // bf16: the f32 scale straight into the f32 products
+      if constexpr (h == 1) *(u32x4*)(rowp[j] + w * 16) = decode8_bf16(job[j].pk[w], S32[j][w < 2 ? 0 : 1]);
     } else {
       const _Float16 S = __builtin_bit_cast(f16x2, S01[j])[w < 2 ? 0 : 1];
       const f16x2 SS = {S, S};
       const uint32_t x = job[j].pk[w];
-      if constexpr (DQ == 2 || DQ == 3) {
+      if constexpr (DQ == 2) {
         if constexpr (h == 1) *(u32x4*)(rowp[j] + w * 16) = decode8<DQ>(x, SS);
       } else {
         chunk[2 * h] = fp4x2_times<2 * h>(x, SS);
