@@ -23,7 +23,9 @@ divided by the step time).  Also reported:
     orders (heaviest first, stream order, request order), and of the
     2048x2048 batch heaviest first and paired (the plan's choice);
   * the decode step, the dequant-placement ablation, the measured achievable
-    peaks, the plan's host time, and the CPU oracle timed on bounded samples.
+    peaks, board power and shader clocks under the prefill and the MFMA-only
+    loop (amd-smi), the plan's host time, and the CPU oracle timed on bounded
+    samples.
 
 Before the W warm-up steps the step runs untimed until the clocks have
 settled (at least SETTLE_MS of back-to-back steps; reported as settle_steps):
@@ -307,6 +309,12 @@ def main():
             got = result["decode"]["achieved_GBps"]
             ach["decode_frac_of_traffic_probe"] = round(got / ach["decode_traffic_1_ahead_GBps"], 4)
         result["achievable"] = ach
+        # board power and clocks under the prefill and the MFMA-only loop
+        # (amd-smi; context for the roofline fraction, see --power)
+        try:
+            result["power"] = power_telemetry(K, W, dev, torch, np, secs=4.0)
+        except Exception as e:  # amd-smi missing or unreadable: report, do not fail
+            result["power"] = {"error": f"{type(e).__name__}: {e}"}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, flops, W, dev, torch, np)
     print(json.dumps(result), flush=True)
@@ -704,8 +712,12 @@ def power_telemetry(K, W, dev, torch, np, secs=6.0, period=0.3):
     def poll():
         while not done.is_set():
             t = time.time()
-            r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True,
-                               timeout=10)
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True,
+                                   timeout=10)
+            except (OSError, subprocess.SubprocessError):
+                done.wait(period)
+                continue
             p = re.search(r'"socket_power":\s*\{\s*"value":\s*(\d+)', r.stdout)
             clk = [int(x) for x in re.findall(r'"gfx_\d+":\s*\{\s*"clk":\s*\{\s*"value":\s*(\d+)', r.stdout)]
             if p and clk:
